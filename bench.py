@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Throughput of the GPT-OSS decode sampling tail on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-sweep]
+
+A step is one tail_forward call (RMSNorm -> lm_head -> top-k -> sampler) over
+one batch of synthetic, seeded inputs already resident in HBM.  The headline
+workload is the GPT-OSS-shaped decode step: gbs 1, H 2880, V 201088, k 256,
+bf16 hidden, sampling at top_k 256, top_p 1, T 1, u 0.5, logits not emitted.
+`value` is tokens/s = gbs * K / (time of K steps), timed with HIP events on
+the stream the library launches on, bracketed by device synchronizations.
+
+Also reported: per-stage times, the lm_head kernel's algorithmic HBM rate
+against the 8 TB/s peak (`roofline`), the same numbers at gbs 8 / 64 / 256
+(`by_gbs`), and the fp64 CPU oracle timed on a bounded sample of the
+headline workload (`cpu_baseline`).  Progress goes to stderr; stdout carries
+exactly one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tail tokens/s at gbs 1/8/64/256, V=201088; lm_head HBM GB/s & MFMA % of peak"
+HBM_PEAK = 8000.0  # GB/s, MI355X HBM3E
+COUNTERS = os.path.join(ROOT, "profiles", "lm_head_gemv_gbs1_counters.md")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.join(ROOT, "decode_sampling_tail_amd", "csrc"))):
+        with open(os.path.join(ROOT, "decode_sampling_tail_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """Per-launch HBM bytes of the gbs-1 lm_head kernel from the committed
+    rocprofv3 counter summary, or None if absent or taken on other sources."""
+    if not os.path.exists(COUNTERS):
+        return None
+    text = open(COUNTERS).read()
+    m = re.search(r"source_hash:\s*(\w+)", text)
+    b = re.search(r"hbm_bytes_per_dispatch:\s*([\d.eE+]+)", text)
+    if not m or not b or m.group(1) != kernel_source_hash():
+        return None
+    return float(b.group(1))
+
+
+def workloads():
+    import synth
+    # (label, config id): the shapes and distributions of the five workloads;
+    # the padded gbs-64 one is timed without its planted ties (timing only)
+    return [("gptoss_tail_gbs1", 1), ("gbs8_sampling", 2), ("gbs64_padded", 3), ("gbs256_dense", 4)]
+
+
+def gpu_inputs(cid, torch, np):
+    import synth
+    inp = synth.make_config(cid)
+    dev = torch.device("cuda")
+    if inp.dtype == synth.DT_BF16:
+        hidden = torch.from_numpy(inp.hidden.view(np.int16)).view(torch.bfloat16)
+    else:
+        hidden = torch.from_numpy(inp.hidden)
+    run = len(inp.params) - 1  # the sampling run of the gbs-1 workload
+    return inp, dict(hidden=hidden.to(dev), gamma=torch.from_numpy(inp.gamma).to(dev),
+                     w_t=torch.from_numpy(inp.w_t.view(np.int16)).view(torch.bfloat16).to(dev),
+                     params=torch.from_numpy(np.ascontiguousarray(inp.params[run])).to(dev)), run
+
+
+def time_loop(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1000.0 / steps  # seconds per call
+
+
+def bench_workload(cid, args, torch, np):
+    import decode_sampling_tail_amd as dst
+    inp, g, run = gpu_inputs(cid, torch, np)
+    f = dst.Forward(inp.gbs, inp.H, inp.V, inp.k, inp.H_u, inp.eps, inp.zero_pad, deferred=True,
+                    emit_logits=False)
+    t_step = time_loop(torch, lambda: f(g["hidden"], g["gamma"], g["w_t"], g["params"]),
+                       args.steps, args.warmup)
+    # stage by stage, same kernels and launch shapes as inside tail_forward
+    y, r = dst.rmsnorm(g["hidden"], g["gamma"], inp.H_u, inp.eps, inp.zero_pad, deferred=True)
+    logits = torch.empty((inp.gbs, inp.V), dtype=torch.float32, device="cuda")
+    vals, idx = dst.topk(dst.lm_head(y, g["w_t"], inp.H_u, inp.zero_pad, row_scale=r, out=logits), inp.k)
+    t_norm = time_loop(torch, lambda: dst.rmsnorm(g["hidden"], g["gamma"], inp.H_u, inp.eps,
+                                                  inp.zero_pad, deferred=True, out_y=y, out_r=r),
+                       args.steps, args.warmup)
+    t_lm = time_loop(torch, lambda: dst.lm_head(y, g["w_t"], inp.H_u, inp.zero_pad, row_scale=r,
+                                                out=logits), args.steps, args.warmup)
+    ws = torch.empty(dst.workspace_size(inp.gbs, 1, 1, inp.V, inp.k, dst.EMIT_LOGITS),
+                     dtype=torch.uint8, device="cuda")
+    t_topk = time_loop(torch, lambda: dst.topk(logits, inp.k, vals, idx, ws), args.steps, args.warmup)
+    tok = torch.empty((inp.gbs,), dtype=torch.int32, device="cuda")
+    t_samp = time_loop(torch, lambda: dst.sample(vals, idx, g["params"], tok), args.steps, args.warmup)
+    w_bytes = inp.H_u * inp.V * 2
+    lm_bytes = w_bytes + inp.gbs * inp.H * 4 + inp.gbs * 4 + inp.gbs * inp.V * 4
+    flops = 2.0 * inp.gbs * inp.H_u * inp.V
+    res = dict(gbs=inp.gbs, tokens_per_s=inp.gbs / t_step, steps_per_s=1.0 / t_step,
+               ms_per_step=t_step * 1e3,
+               stage_us=dict(rmsnorm=t_norm * 1e6, lm_head=t_lm * 1e6, topk=t_topk * 1e6,
+                             sample=t_samp * 1e6),
+               lm_head_gbs=lm_bytes / t_lm / 1e9, lm_head_tflops=flops / t_lm / 1e12,
+               lm_head_bytes=lm_bytes)
+    del g, f, logits, ws
+    torch.cuda.empty_cache()
+    return inp, run, res
+
+
+def cpu_baseline(inp, run, budget_s=12.0):
+    """The fp64 oracle, as it stands, on whole tail steps of the headline workload."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.tail(inp.hidden, inp.dtype, inp.gamma, inp.w_t, inp.H_u, inp.k, inp.eps, inp.zero_pad,
+                    params=inp.params[run])
+        n += 1
+        el = time.perf_counter() - t0
+        log(f"cpu oracle step {n}: {el:.1f} s")
+        if el >= budget_s or n >= 20:
+            break
+    return dict(value=n * inp.gbs / el, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{n} whole tail steps (fp64 RMSNorm, fp64 lm_head, full stable sort, "
+                       f"fp64 sampler) of the gbs {inp.gbs} workload, {el:.1f} s")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the tail runs with the whole vocabulary on one device)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.init()
+
+    results = {}
+    head_inp = head_run = None
+    for label, cid in workloads():
+        if args.no_sweep and cid != 1:
+            continue
+        log(f"workload {label}: generating inputs and timing {args.steps} steps")
+        inp, run, res = bench_workload(cid, args, torch, np)
+        log(f"{label}: {res['tokens_per_s']:.1f} tok/s, {res['ms_per_step']:.3f} ms/step, "
+            f"lm_head {res['lm_head_gbs']:.0f} GB/s, stages {res['stage_us']}")
+        results[label] = res
+        if cid == 1:
+            head_inp, head_run = inp, run
+
+    head = results["gptoss_tail_gbs1"]
+    traffic = counter_traffic()
+    roof = dict(bound="hbm", achieved=head["lm_head_gbs"], peak=HBM_PEAK, unit="GB/s",
+                frac=head["lm_head_gbs"] / HBM_PEAK, traffic=traffic,
+                kernel="lm_head gemv (gbs 1)", bytes_per_launch=head["lm_head_bytes"],
+                launch_us=head["stage_us"]["lm_head"])
+    out = dict(metric=METRIC, value=head["tokens_per_s"], unit="tokens/s", n_gpus=1,
+               steps=args.steps, warmup=args.warmup, ms_per_step=head["ms_per_step"],
+               higher_is_better=True, scaling="weak", vs_baseline=None, dtype="fp32",
+               data="synthetic",
+               config=dict(workload="gptoss_tail_gbs1", gbs=1, H=2880, H_u=2880, V=201088, k=256,
+                           hidden_dtype="bf16", weight_dtype="bf16",
+                           sampling="top_k=256 top_p=1 T=1 u=0.5", emit_logits=False,
+                           parallelism="none (one GPU, whole vocabulary)"),
+               stage_us=head["stage_us"], roofline=roof,
+               by_gbs={lbl: dict(gbs=r["gbs"], tokens_per_s=r["tokens_per_s"], ms_per_step=r["ms_per_step"],
+                                 lm_head_gbs=r["lm_head_gbs"], lm_head_hbm_frac=r["lm_head_gbs"] / HBM_PEAK,
+                                 lm_head_tflops=r["lm_head_tflops"], stage_us=r["stage_us"])
+                       for lbl, r in results.items()},
+               source_hash=kernel_source_hash())
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle on the headline workload")
+        out["cpu_baseline"] = cpu_baseline(head_inp, head_run)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

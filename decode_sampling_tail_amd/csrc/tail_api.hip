@@ -1,0 +1,210 @@
+// Host side of the decode-tail C ABI: argument validation (pure host logic,
+// run before any HIP call), workspace layout and kernel dispatch.  The entry
+// points and their contracts are declared in include/tail.h.
+#include "../../include/tail.h"
+#include "tail_internal.h"
+
+#include <math.h>
+
+#define TAIL_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using tail::align256;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t dtype_bytes(int dtype) { return dtype == TAIL_F32 ? 4 : 2; }
+
+// Stride s of the interleaved pad lanes (0 when there are none to skip), or
+// -1 when the padding geometry is invalid.
+int pad_stride(int H, int H_u, unsigned flags) {
+  if (!(flags & TAIL_ZERO_PAD) || H == H_u) return 0;
+  int npad = H - H_u;
+  if (H % npad != 0) return -1;
+  int s = H / npad;
+  return s >= 2 ? s : -1;
+}
+
+int check_shape(int gbs, int H, int H_u) {
+  if (gbs < 1 || H < 1 || H_u < 1 || H_u > H) return TAIL_ERR_INVALID_ARG;
+  if (gbs > TAIL_GBS_MAX || H > TAIL_H_MAX) return TAIL_ERR_UNSUPPORTED;
+  return TAIL_OK;
+}
+
+int check_vocab(int V) {
+  if (V < 1) return TAIL_ERR_INVALID_ARG;
+  if (V % 8 != 0) return TAIL_ERR_UNSUPPORTED;  // 16-byte weight rows
+  return TAIL_OK;
+}
+
+int check_k(int V, int k) {
+  if (k < 1 || k > V) return TAIL_ERR_INVALID_ARG;
+  if (k > TAIL_K_MAX) return TAIL_ERR_UNSUPPORTED;
+  tail::TopkGeom g;
+  if (!tail::topk_geometry(V, k, &g)) return TAIL_ERR_UNSUPPORTED;
+  return TAIL_OK;
+}
+
+struct FwdLayout {
+  size_t y, r, logits, gkey, total;
+};
+
+FwdLayout forward_layout(int gbs, int H, int V, int k, unsigned flags) {
+  tail::TopkGeom g;
+  tail::topk_geometry(V, k, &g);
+  FwdLayout L;
+  size_t off = 0;
+  L.y = off;
+  off = align256(off + size_t(gbs) * H * 4);
+  L.r = off;
+  off = align256(off + size_t(gbs) * 4);
+  L.logits = off;
+  if (!(flags & TAIL_EMIT_LOGITS)) off = align256(off + size_t(gbs) * V * 4);
+  L.gkey = off;
+  off = align256(off + size_t(gbs) * g.groups * 4);
+  L.total = off;
+  return L;
+}
+
+size_t topk_ws_bytes(int gbs, int V, int k) {
+  tail::TopkGeom g;
+  tail::topk_geometry(V, k, &g);
+  return align256(size_t(gbs) * g.groups * 4);
+}
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return TAIL_OK;
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < need) return TAIL_ERR_WORKSPACE;
+  return TAIL_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TAIL_OK : TAIL_ERR_HIP; }
+
+}  // namespace
+
+TAIL_API const char* tail_status_string(int status) {
+  switch (status) {
+    case TAIL_OK: return "ok";
+    case TAIL_ERR_INVALID_ARG: return "invalid argument";
+    case TAIL_ERR_UNSUPPORTED: return "unsupported by this build";
+    case TAIL_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case TAIL_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+TAIL_API size_t tail_workspace_size(int gbs, int H, int H_u, int V, int k, unsigned flags) {
+  if (check_shape(gbs, H, H_u) || check_vocab(V) || check_k(V, k)) return 0;
+  if (pad_stride(H, H_u, flags) < 0) return 0;
+  size_t fwd = forward_layout(gbs, H, V, k, flags).total;
+  size_t tk = topk_ws_bytes(gbs, V, k);
+  return fwd > tk ? fwd : tk;
+}
+
+TAIL_API int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int H,
+                          int H_u, float eps, unsigned flags, float* out_y, float* out_r,
+                          void* stream) {
+  if (int s = check_shape(gbs, H, H_u)) return s;
+  if (dtype != TAIL_F32 && dtype != TAIL_F16 && dtype != TAIL_BF16) return TAIL_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return TAIL_ERR_INVALID_ARG;
+  if (flags & ~(TAIL_EMIT_LOGITS | TAIL_ZERO_PAD | TAIL_DEFERRED_RMS)) return TAIL_ERR_INVALID_ARG;
+  int ps = pad_stride(H, H_u, flags);
+  if (ps < 0) return TAIL_ERR_INVALID_ARG;
+  bool deferred = flags & TAIL_DEFERRED_RMS;
+  if (!hidden || !gamma || !out_y || (deferred && !out_r)) return TAIL_ERR_INVALID_ARG;
+  if (!aligned(hidden, dtype_bytes(dtype)) || !aligned(gamma, 4) || !aligned(out_y, 4) ||
+      (out_r && !aligned(out_r, 4)))
+    return TAIL_ERR_INVALID_ARG;
+  return hip_status(tail::launch_rmsnorm(hidden, dtype, gamma, gbs, H, H_u, ps, eps, deferred,
+                                         out_y, out_r, (hipStream_t)stream));
+}
+
+TAIL_API int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_scale, int gbs,
+                          int H, int H_u, int V, unsigned flags, float* logits, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (int s = check_shape(gbs, H, H_u)) return s;
+  if (int s = check_vocab(V)) return s;
+  if (flags & ~(TAIL_EMIT_LOGITS | TAIL_ZERO_PAD | TAIL_DEFERRED_RMS)) return TAIL_ERR_INVALID_ARG;
+  int ps = pad_stride(H, H_u, flags);
+  if (ps < 0) return TAIL_ERR_INVALID_ARG;
+  if (!y || !w_t || !logits) return TAIL_ERR_INVALID_ARG;
+  if (!aligned(y, 4) || !aligned(w_t, 16) || !aligned(logits, 16) ||
+      (row_scale && !aligned(row_scale, 4)))
+    return TAIL_ERR_INVALID_ARG;
+  (void)ws;
+  (void)ws_bytes;  // this path needs no workspace
+  // without pad skipping every lane of the hidden is used
+  int H_used = ps ? H_u : H;
+  return hip_status(tail::launch_lm_head_gemv(y, H, w_t, row_scale, gbs, H_used, ps, V, logits,
+                                              (hipStream_t)stream));
+}
+
+TAIL_API int tail_topk(const float* logits, int gbs, int V, int k, float* vals, int32_t* idx,
+                       void* ws, size_t ws_bytes, void* stream) {
+  if (gbs < 1) return TAIL_ERR_INVALID_ARG;
+  if (gbs > TAIL_GBS_MAX) return TAIL_ERR_UNSUPPORTED;
+  if (int s = check_vocab(V)) return s;
+  if (int s = check_k(V, k)) return s;
+  if (!logits || !vals || !idx) return TAIL_ERR_INVALID_ARG;
+  if (!aligned(logits, 16) || !aligned(vals, 4) || !aligned(idx, 4)) return TAIL_ERR_INVALID_ARG;
+  if (int s = check_ws(ws, ws_bytes, topk_ws_bytes(gbs, V, k))) return s;
+  tail::TopkGeom g;
+  tail::topk_geometry(V, k, &g);
+  return hip_status(tail::launch_topk(logits, gbs, V, k, g, (uint32_t*)ws, vals, idx,
+                                      (hipStream_t)stream));
+}
+
+TAIL_API int tail_sample(const float* vals, const int32_t* idx, int gbs, int k,
+                         const float* params, int ncols, int32_t* tokens, void* stream) {
+  if (gbs < 1 || k < 1) return TAIL_ERR_INVALID_ARG;
+  if (gbs > TAIL_GBS_MAX || k > TAIL_K_MAX) return TAIL_ERR_UNSUPPORTED;
+  if (ncols != 3 && ncols != 4) return TAIL_ERR_INVALID_ARG;
+  if (!vals || !idx || !params || !tokens) return TAIL_ERR_INVALID_ARG;
+  if (!aligned(vals, 4) || !aligned(idx, 4) || !aligned(params, 4) || !aligned(tokens, 4))
+    return TAIL_ERR_INVALID_ARG;
+  return hip_status(
+      tail::launch_sample(vals, idx, gbs, k, params, ncols, tokens, (hipStream_t)stream));
+}
+
+TAIL_API int tail_forward(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t,
+                          int gbs, int H, int H_u, int V, int k, float eps, unsigned flags,
+                          const float* params, int ncols, float* logits, float* vals, int32_t* idx,
+                          int32_t* tokens, void* ws, size_t ws_bytes, void* stream) {
+  if (int s = check_shape(gbs, H, H_u)) return s;
+  if (int s = check_vocab(V)) return s;
+  if (int s = check_k(V, k)) return s;
+  if (dtype != TAIL_F32 && dtype != TAIL_F16 && dtype != TAIL_BF16) return TAIL_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return TAIL_ERR_INVALID_ARG;
+  if (flags & ~(TAIL_EMIT_LOGITS | TAIL_ZERO_PAD | TAIL_DEFERRED_RMS)) return TAIL_ERR_INVALID_ARG;
+  int ps = pad_stride(H, H_u, flags);
+  if (ps < 0) return TAIL_ERR_INVALID_ARG;
+  bool emit = flags & TAIL_EMIT_LOGITS;
+  if (!hidden || !gamma || !w_t || !vals || !idx) return TAIL_ERR_INVALID_ARG;
+  if (emit && !logits) return TAIL_ERR_INVALID_ARG;
+  if (params && (ncols != 3 && ncols != 4)) return TAIL_ERR_INVALID_ARG;
+  if (params && !tokens) return TAIL_ERR_INVALID_ARG;
+  if (!aligned(hidden, dtype_bytes(dtype)) || !aligned(gamma, 4) || !aligned(w_t, 16) ||
+      !aligned(vals, 4) || !aligned(idx, 4) || (emit && !aligned(logits, 16)) ||
+      (params && (!aligned(params, 4) || !aligned(tokens, 4))))
+    return TAIL_ERR_INVALID_ARG;
+  FwdLayout L = forward_layout(gbs, H, V, k, flags);
+  if (int s = check_ws(ws, ws_bytes, L.total)) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)ws;
+  float* y = (float*)(base + L.y);
+  float* r = (float*)(base + L.r);
+  float* lg = emit ? logits : (float*)(base + L.logits);
+  uint32_t* gk = (uint32_t*)(base + L.gkey);
+  bool deferred = flags & TAIL_DEFERRED_RMS;
+  tail::TopkGeom g;
+  tail::topk_geometry(V, k, &g);
+  hipError_t e = tail::launch_rmsnorm(hidden, dtype, gamma, gbs, H, H_u, ps, eps, deferred, y, r, st);
+  if (e == hipSuccess)
+    e = tail::launch_lm_head_gemv(y, H, w_t, deferred ? r : nullptr, gbs, ps ? H_u : H, ps, V, lg, st);
+  if (e == hipSuccess) e = tail::launch_topk(lg, gbs, V, k, g, gk, vals, idx, st);
+  if (e == hipSuccess && params)
+    e = tail::launch_sample(vals, idx, gbs, k, params, ncols, tokens, st);
+  return hip_status(e);
+}

@@ -1,0 +1,174 @@
+/*
+ * decode_sampling_tail -- C ABI of the GPT-OSS decode sampling tail on one
+ * MI355X (gfx950): final RMSNorm -> bf16 lm_head -> top-k -> sampler.
+ *
+ * The operations and their parameters follow the page "GPT-OSS Tail Chunked
+ * Megakernel Kernel API Reference" (NKI library docs), cited below by the
+ * name of the parameter whose paragraph defines them.  Everything runs on
+ * one GPU with the whole vocabulary local, so the page's vocabulary shards,
+ * collectives and rank maps have no counterpart here (V_s = V).
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers, allocated, owned and freed by the
+ *    caller.  The library allocates nothing, keeps no mutable global state,
+ *    never synchronizes, and enqueues its kernels on `stream` (a hipStream_t
+ *    passed as void*; NULL = the default stream).  Outputs are valid once the
+ *    stream reaches that point.
+ *  - Arrays are C-contiguous (row-major) with the shapes given.
+ *  - Every call validates its arguments on the host BEFORE any HIP call and
+ *    returns a status code; on an error nothing is enqueued and no output is
+ *    touched.  TAIL_ERR_HIP reports a launch error from the HIP runtime.
+ *    Faults inside a kernel surface asynchronously, as for any HIP call.
+ *  - Results are deterministic: the same inputs give the same bytes, and a
+ *    logit never depends on the column's position or on the other rows of
+ *    the batch within one lm_head path (no floating-point atomics).
+ *  - Calls on different streams may run concurrently as long as they do not
+ *    share output or workspace memory.
+ */
+#ifndef DECODE_SAMPLING_TAIL_H
+#define DECODE_SAMPLING_TAIL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define TAIL_OK 0
+#define TAIL_ERR_INVALID_ARG 1 /* a size, pointer, flag or dtype is out of its domain */
+#define TAIL_ERR_UNSUPPORTED 2 /* valid, but outside what this build implements */
+#define TAIL_ERR_WORKSPACE 3   /* workspace missing, misaligned or too small */
+#define TAIL_ERR_HIP 4         /* the HIP runtime rejected a launch */
+
+/* storage dtype of hidden_states ("hidden_states": fp32, fp16 or bf16) */
+#define TAIL_F32 0
+#define TAIL_F16 1
+#define TAIL_BF16 2
+
+/* flags (run-time counterparts of the page's trace-time flags) */
+#define TAIL_EMIT_LOGITS 1u  /* "emit_logits": write the fp32 [gbs,V] logits */
+#define TAIL_ZERO_PAD 2u     /* "zero_interleaved_pad": skip the interleaved pad lanes */
+#define TAIL_DEFERRED_RMS 4u /* "deferred_rms": apply the row's rms scale after the contraction */
+
+/* limits of this build */
+#define TAIL_K_MAX 1024      /* largest k ("k": 256 in production) */
+#define TAIL_GBS_MAX 4096    /* largest batch */
+#define TAIL_H_MAX 65536     /* largest hidden width */
+
+/*
+ * Pad lanes ("zero_interleaved_pad", "hidden_actual").  With TAIL_ZERO_PAD and
+ * H > H_u, the hidden is split into groups of s = H / (H - H_u) lanes and the
+ * LAST lane of every group is a pad lane (H must be a multiple of H - H_u).
+ * Pad lanes of hidden, gamma and of the weight's rows are never read, so any
+ * value there (NaN included) cannot reach an output.  Without the flag all H
+ * lanes are used and the caller guarantees that padding holds zeros.  The
+ * mean square of the RMSNorm always divides by H_u (H_u = H when unpadded).
+ */
+
+/*
+ * tail_rmsnorm -- final RMSNorm ("gamma", "eps", "hidden_actual",
+ * "hidden_states", "deferred_rms").
+ *
+ *   hidden [gbs, H]  dtype TAIL_F32 / TAIL_F16 / TAIL_BF16 (bf16 as raw uint16
+ *                    bits); widened exactly to fp32 (the page's 16-bit input
+ *                    path), so a 16-bit input gives the same bytes as its
+ *                    pre-widened fp32 copy.  Naturally aligned.
+ *   gamma  [H]       fp32.
+ *   eps              >= 0, added to the mean square inside the square root.
+ *   out_y  [gbs, H]  fp32: x * r * gamma ("(x*rms)*gamma" order), or x * gamma
+ *                    with TAIL_DEFERRED_RMS; pad lanes are written as 0.
+ *   out_r  [gbs]     fp32: r = 1/sqrt(mean_{H_u}(x^2) + eps); may be NULL
+ *                    unless TAIL_DEFERRED_RMS is set.
+ * Only TAIL_ZERO_PAD and TAIL_DEFERRED_RMS are meaningful in `flags`.
+ */
+int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int H, int H_u,
+                 float eps, unsigned flags, float* out_y, float* out_r, void* stream);
+
+/*
+ * tail_lm_head -- the lm_head contraction ("lm_head_weight_t", "emit_logits").
+ *
+ *   y         [gbs, H] fp32 normalized hidden rows (the output of tail_rmsnorm).
+ *   w_t       [H, V]   bf16 raw bits, ALREADY TRANSPOSED and C-contiguous (V is
+ *                      the fast axis), 16-byte aligned; V must be a multiple
+ *                      of 8 (TAIL_ERR_UNSUPPORTED otherwise).
+ *   row_scale [gbs]    fp32 per-row factor applied to the finished sum (the
+ *                      deferred rms scale), or NULL for none.
+ *   logits    [gbs, V] fp32, 16-byte aligned:
+ *                      logits[b,v] = row_scale[b] * sum_h y[b,h] * W[h,v],
+ *                      the sum in fp32 over the real (non-pad) lanes with
+ *                      full-precision fp32 activations (the activations are
+ *                      never rounded to bf16).
+ *   ws, ws_bytes       workspace of at least tail_workspace_size() bytes,
+ *                      256-byte aligned (may be NULL when that size is 0).
+ * Only TAIL_ZERO_PAD is meaningful in `flags`.
+ */
+int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_scale, int gbs, int H,
+                 int H_u, int V, unsigned flags, float* logits, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/*
+ * tail_topk -- global top-k of every row over the full vocabulary ("k",
+ * Background: the global top-k computed locally over the full vocabulary).
+ *
+ *   logits [gbs, V] fp32, finite (NaN ordering is unspecified), 16-byte aligned.
+ *   vals   [gbs, k] fp32: the k largest logits of the row, descending.
+ *   idx    [gbs, k] int32: their column indices.  Equal values are listed in
+ *                   ascending index order, so ties at the k-th place keep the
+ *                   lower indices; -0.0 and +0.0 are equal.
+ *   1 <= k <= min(V, TAIL_K_MAX).
+ */
+int tail_topk(const float* logits, int gbs, int V, int k, float* vals, int32_t* idx, void* ws,
+              size_t ws_bytes, void* stream);
+
+/*
+ * tail_sample -- per-row sampler over the k candidates ("sampling_params").
+ *
+ *   vals, idx  [gbs, k] as produced by tail_topk (descending).
+ *   params     [gbs, ncols] fp32, ncols 3 = [top_k, top_p, temperature] with
+ *              the deterministic draw u = 0.5, or 4 = [.., u] with u in [0,1).
+ *   tokens     [gbs] int32: the sampled column index.
+ * Per row: kk = trunc(top_k), and kk = k when top_k is not in [1, k+1);
+ * temperature <= 0 (or NaN) is greedy: tokens = idx[0].  Otherwise, in fp64,
+ * e_i = exp((vals_i - vals_0) / T) for i < kk, S_i = e_0 + .. + e_i; the
+ * nucleus keeps m = 1 + min{i : S_i >= top_p * S_{kk-1}} candidates (kk when
+ * none); the token is idx[j] with j = min{i < m : S_i > u * S_{m-1}} (m-1 when
+ * none), i.e. candidate i owns [S_{i-1}, S_i) / S_{m-1}.  u < 0 acts as 0.
+ */
+int tail_sample(const float* vals, const int32_t* idx, int gbs, int k, const float* params,
+                int ncols, int32_t* tokens, void* stream);
+
+/*
+ * tail_forward -- the whole tail in one call (the page's
+ * gpt_oss_tail_chunked_megakernel on one GPU): RMSNorm -> lm_head -> top-k ->
+ * sampler, all enqueued on `stream`.
+ *
+ *   hidden, dtype, gamma, w_t, gbs, H, H_u, V, k, eps: as above.
+ *   flags:  TAIL_EMIT_LOGITS (write `logits`), TAIL_ZERO_PAD, TAIL_DEFERRED_RMS.
+ *   params: [gbs, ncols] or NULL; NULL skips the sampler and leaves `tokens`
+ *           untouched (tokens may then be NULL).
+ *   logits: [gbs, V] fp32, required only with TAIL_EMIT_LOGITS.
+ *   vals, idx: [gbs, k] top-k outputs (always written).
+ *   ws:     workspace of at least tail_workspace_size(...) bytes, 256-byte aligned.
+ */
+int tail_forward(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t, int gbs,
+                 int H, int H_u, int V, int k, float eps, unsigned flags, const float* params,
+                 int ncols, float* logits, float* vals, int32_t* idx, int32_t* tokens, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/*
+ * Workspace bytes needed by tail_forward, tail_lm_head and tail_topk for these
+ * sizes and flags (one buffer of this size serves any of them).  Returns 0
+ * for arguments that the calls would reject.  Pure host function.
+ */
+size_t tail_workspace_size(int gbs, int H, int H_u, int V, int k, unsigned flags);
+
+/* Static description of a status code (never NULL). */
+const char* tail_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_SAMPLING_TAIL_H */

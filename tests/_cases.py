@@ -1,0 +1,208 @@
+"""Shared helpers of the GPU parity tests: workloads, oracle runs (cached per
+process), the tie planting of the padded workload, and the comparison rules.
+
+Comparison rules (tolerances of the parity bar):
+* logits: per row, relative L2 error <= 1e-5 and max abs error <= 2e-3
+  against the fp64 oracle;
+* top-k: the GPU's k indices contain every column whose oracle logit is
+  above t + 1e-4 and none below t - 1e-4 (t: the oracle's k-th value), and the
+  GPU list equals, exactly, the oracle's top-k of the GPU's own logits;
+* tokens: equal to the oracle's, except rows the oracle marks ambiguous
+  (u within `band` of a CDF boundary or of the nucleus cut, or a logit gap
+  below 1e-4 at a boundary that decides the token).  `band` is 1e-6, widened
+  per row to the CDF movement that the row's measured logit error can cause
+  (4 * eps / T, eps = max |logit error| among the candidates); the widened
+  rows are counted and reported.  Separately, the oracle's sampler applied
+  to the GPU's own candidates must give the GPU's token except within 1e-6
+  of a boundary.
+"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+
+import oracle
+import synth
+
+REL_L2 = 1e-5
+MAX_ABS = 2e-3
+TIE_GAP = 1e-4
+CDF_BAND = 1e-6
+
+
+# ------------------------------------------------------------------ workloads
+@functools.lru_cache(maxsize=None)
+def config(cid: int) -> synth.TailInputs:
+    inp = synth.make_config(cid)
+    if cid == 3:
+        plant_ties(inp)
+    return inp
+
+
+def plant_ties(inp: synth.TailInputs) -> None:
+    """Plant exact logit ties at the top-k boundary of the padded workload:
+    256 source columns near oracle rank k (ranks k-1..k+2 of each row, then
+    further ranks to fill), each copied onto a distinct target column that no
+    row ranks in its top 4096, so 512 columns form 256 duplicated pairs."""
+    ref = oracle_tail(inp, planted=False)
+    order = np.argsort(-ref["logits"], axis=1, kind="stable")
+    k = inp.k
+    sources: list[int] = []
+    seen = set()
+    for lo, hi in ((k - 2, k + 2), (k + 2, 4096)):
+        for r in range(lo, hi):
+            for b in range(inp.gbs):
+                c = int(order[b, r])
+                if c not in seen and len(sources) < 256:
+                    seen.add(c)
+                    sources.append(c)
+        if len(sources) >= 256:
+            break
+    top = np.zeros(inp.V, bool)
+    top[order[:, :4096].ravel()] = True
+    cand = np.nonzero(~top)[0]
+    targets = synth.tie_targets(3, cand, len(sources))
+    synth.duplicate_columns(inp.w_t, np.array(sources), targets)
+    inp.tie_pairs = np.stack([np.array(sources), targets], axis=1)
+
+
+_oracle_cache: dict = {}
+
+
+def oracle_tail(inp: synth.TailInputs, run: int = 0, planted: bool = True, rows=None):
+    key = (inp.name, run, planted, None if rows is None else tuple(rows))
+    if key not in _oracle_cache:
+        params = inp.params[run] if inp.params else None
+        out = oracle.tail(inp.hidden, inp.dtype, inp.gamma, inp.w_t, inp.H_u, inp.k, inp.eps,
+                          inp.zero_pad, params=params, rows=rows)
+        out["vals_k1"] = oracle.topk(out["logits"], inp.k + 1)[0] if inp.k < inp.V else None
+        _oracle_cache[key] = out
+    return _oracle_cache[key]
+
+
+# ------------------------------------------------------------------- GPU side
+def to_gpu(inp: synth.TailInputs, device="cuda"):
+    import torch
+    if inp.dtype == synth.DT_BF16:
+        hidden = torch.from_numpy(inp.hidden.view(np.int16)).view(torch.bfloat16)
+    else:
+        hidden = torch.from_numpy(inp.hidden)
+    d = dict(hidden=hidden.to(device),
+             gamma=torch.from_numpy(inp.gamma).to(device),
+             w_t=torch.from_numpy(inp.w_t.view(np.int16)).view(torch.bfloat16).to(device),
+             params=[torch.from_numpy(np.ascontiguousarray(p)).to(device) for p in inp.params])
+    return d
+
+
+# ---------------------------------------------------------------- comparisons
+def logit_errors(L_gpu: np.ndarray, L_ref: np.ndarray):
+    d = L_gpu.astype(np.float64) - L_ref
+    rel = np.linalg.norm(d, axis=1) / np.linalg.norm(L_ref, axis=1)
+    mx = np.max(np.abs(d), axis=1)
+    return rel, mx
+
+
+def check_logits(L_gpu, L_ref):
+    rel, mx = logit_errors(L_gpu, L_ref)
+    bad = np.nonzero((rel > REL_L2) | (mx > MAX_ABS))[0]
+    return [f"row {b}: rel-L2 {rel[b]:.3e} max-abs {mx[b]:.3e}" for b in bad[:5]], rel, mx
+
+
+def check_topk_sets(idx_gpu, L_ref, k):
+    """GPU set contains {L > t + gap} and avoids {L < t - gap} per row."""
+    fails = []
+    for b in range(L_ref.shape[0]):
+        t = np.sort(L_ref[b])[::-1][k - 1]
+        got = set(int(i) for i in idx_gpu[b])
+        must = set(np.nonzero(L_ref[b] > t + TIE_GAP)[0].tolist())
+        never = set(np.nonzero(L_ref[b] < t - TIE_GAP)[0].tolist())
+        if not must <= got:
+            fails.append(f"row {b}: missing {sorted(must - got)[:5]}")
+        if got & never:
+            fails.append(f"row {b}: extra {sorted(got & never)[:5]}")
+    return fails
+
+
+def check_topk_exact(vals_gpu, idx_gpu, L_gpu, k):
+    """The GPU list equals the oracle's top-k of the GPU's own logits."""
+    ov, oi = oracle.topk(L_gpu.astype(np.float64), k)
+    fails = []
+    for b in range(L_gpu.shape[0]):
+        if not np.array_equal(oi[b], idx_gpu[b].astype(np.int64)):
+            j = int(np.argmax(oi[b] != idx_gpu[b]))
+            fails.append(f"row {b}: idx differs first at rank {j}: {oi[b][j]} vs {idx_gpu[b][j]}")
+        elif not np.array_equal(ov[b], vals_gpu[b].astype(np.float64)):
+            fails.append(f"row {b}: values differ")
+    return fails
+
+
+def _near_cdf(diag, u, top_p, band):
+    if diag["greedy"]:
+        return False
+    Q, C, m = diag["Q"], diag["C"], diag["m"]
+    if np.min(np.abs(Q[:-1] - u)) < band if len(Q) > 1 else False:
+        return True
+    if abs(C[m - 1] - top_p) < band or (m >= 2 and abs(C[m - 2] - top_p) < band):
+        return True
+    return False
+
+
+def token_exemption(diag, vals_ref, vals_k1, u, top_p, T, k, band):
+    """Why the oracle cannot pin this row's token (empty string: it can)."""
+    if diag["greedy"]:
+        return "greedy near-tie" if vals_ref[0] - vals_ref[1] < TIE_GAP else ""
+    if _near_cdf(diag, u, top_p, band):
+        return "u or top_p within band of a boundary"
+    kk, m, Q = diag["kk"], diag["m"], diag["Q"]
+    if kk < k and vals_ref[kk - 1] - vals_ref[kk] < TIE_GAP:
+        return "near-tie at the top_k cut"
+    if kk == k and vals_k1 is not None and vals_ref[k - 1] - vals_k1 < TIE_GAP:
+        return "near-tie at the k cut"
+    if m < kk and vals_ref[m - 1] - vals_ref[m] < TIE_GAP:
+        return "near-tie at the nucleus cut"
+    for i in range(m - 1):
+        if vals_ref[i] - vals_ref[i + 1] < TIE_GAP:
+            lo = Q[i - 1] if i > 0 else 0.0
+            if lo - band <= u < Q[i + 1] + band:
+                return "near-tie pair holds u"
+    return ""
+
+
+def check_tokens(tok_gpu, ref, params, L_gpu, k):
+    """End-to-end tokens vs the oracle; returns (fails, exempt_rows, widened_rows)."""
+    fails, exempt, widened = [], [], []
+    for b in range(len(tok_gpu)):
+        d = ref["diag"][b]
+        u = float(params[b, 3]) if params.shape[1] == 4 else oracle.DETERMINISTIC_DRAW
+        top_p, T = float(params[b, 1]), float(params[b, 2])
+        if int(tok_gpu[b]) == int(ref["tokens"][b]):
+            continue
+        cand = ref["idx"][b]
+        eps_row = float(np.max(np.abs(L_gpu[b, cand].astype(np.float64) - ref["vals"][b])))
+        why = token_exemption(d, ref["vals"][b], None if ref["vals_k1"] is None else ref["vals_k1"][b][k],
+                              u, top_p, T, k, CDF_BAND)
+        if why:
+            exempt.append((b, why))
+            continue
+        band = max(CDF_BAND, 4.0 * eps_row / T) if T > 0 else CDF_BAND
+        why = token_exemption(d, ref["vals"][b], None if ref["vals_k1"] is None else ref["vals_k1"][b][k],
+                              u, top_p, T, k, band)
+        if why:
+            widened.append((b, why, band))
+            continue
+        fails.append(f"row {b}: token {int(tok_gpu[b])} vs oracle {int(ref['tokens'][b])}")
+    return fails, exempt, widened
+
+
+def check_sampler_on_gpu_candidates(tok_gpu, vals_gpu, idx_gpu, params):
+    """The oracle sampler on the GPU's own candidates reproduces the GPU token."""
+    toks, diags = oracle.sample(vals_gpu.astype(np.float64), idx_gpu.astype(np.int64), params)
+    fails = []
+    for b in range(len(tok_gpu)):
+        if int(toks[b]) == int(tok_gpu[b]):
+            continue
+        u = float(params[b, 3]) if params.shape[1] == 4 else oracle.DETERMINISTIC_DRAW
+        if not _near_cdf(diags[b], u, float(params[b, 1]), CDF_BAND):
+            fails.append(f"row {b}: sampler {int(tok_gpu[b])} vs oracle-on-gpu-candidates {int(toks[b])}")
+    return fails

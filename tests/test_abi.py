@@ -1,0 +1,198 @@
+"""The C ABI on the host: the library loads, exports exactly what
+include/tail.h declares, and every invalid argument is rejected with its
+status code before any HIP call (fake, never-dereferenced device pointers
+are enough for that, so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import decode_sampling_tail_amd as dst
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tail.h")
+
+P = ctypes.c_void_p(0x100000)      # 256-byte aligned fake device pointer
+P2 = ctypes.c_void_p(0x200002)     # 2-byte aligned only
+NULL = None
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tail_\w+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    names = declared()
+    assert set(names) == set(dst.EXPORTS)
+    L = dst.lib()
+    for n in names:
+        assert hasattr(L, n)
+    out = subprocess.run(["nm", "-D", "--defined-only", dst.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r"\bT (tail_\w+)", out)))
+    assert exported == names
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (TAIL_\w+) (\d+)u?", text))
+    assert int(consts["TAIL_OK"]) == dst.OK
+    assert int(consts["TAIL_ERR_WORKSPACE"]) == dst.ERR_WORKSPACE
+    assert int(consts["TAIL_BF16"]) == dst.BF16
+    assert int(consts["TAIL_ZERO_PAD"]) == dst.ZERO_PAD
+    assert int(consts["TAIL_DEFERRED_RMS"]) == dst.DEFERRED_RMS
+    assert int(consts["TAIL_EMIT_LOGITS"]) == dst.EMIT_LOGITS
+    assert int(consts["TAIL_K_MAX"]) == dst.K_MAX
+
+
+def test_status_strings_total():
+    for s in range(-2, 8):
+        assert isinstance(dst.status_string(s), str) and dst.status_string(s)
+    assert dst.status_string(dst.ERR_WORKSPACE).startswith("workspace")
+
+
+def rms(**kw):
+    a = dict(hidden=P, dtype=dst.F32, gamma=P, gbs=1, H=16, H_u=16, eps=1e-5, flags=0, y=P, r=P)
+    a.update(kw)
+    return dst.lib().tail_rmsnorm(a["hidden"], a["dtype"], a["gamma"], a["gbs"], a["H"], a["H_u"],
+                                  a["eps"], a["flags"], a["y"], a["r"], None)
+
+
+def test_rmsnorm_validation():
+    E = dst.ERR_INVALID_ARG
+    assert rms(gbs=0) == E
+    assert rms(H=0) == E
+    assert rms(H_u=17) == E
+    assert rms(H_u=0) == E
+    assert rms(dtype=3) == E
+    assert rms(eps=-1.0) == E
+    assert rms(eps=float("nan")) == E
+    assert rms(eps=float("inf")) == E
+    assert rms(hidden=NULL) == E
+    assert rms(gamma=NULL) == E
+    assert rms(y=NULL) == E
+    assert rms(flags=dst.DEFERRED_RMS, r=NULL) == E
+    assert rms(flags=64) == E
+    assert rms(H=3072, H_u=2881, flags=dst.ZERO_PAD) == E      # 191 pad lanes do not divide 3072
+    assert rms(H=3, H_u=1, flags=dst.ZERO_PAD) == E            # 2 pad lanes of 3 do not divide
+    assert rms(hidden=P2, dtype=dst.F32) == E                  # fp32 rows need 4-byte alignment
+    assert rms(gbs=dst.GBS_MAX + 1) == dst.ERR_UNSUPPORTED
+    assert rms(H=dst.H_MAX + 1, H_u=10) == dst.ERR_UNSUPPORTED
+
+
+def test_rmsnorm_pad_stride_two_is_valid_geometry():
+    # H = 4, H_u = 2: groups of s = 2 lanes, lanes 1 and 3 are pad -- valid.  Only
+    # the validation verdict is checked here: a valid call would launch, so it is
+    # made invalid afterwards by a null output to stop before any HIP call.
+    assert rms(H=4, H_u=2, flags=dst.ZERO_PAD, y=NULL) == dst.ERR_INVALID_ARG
+
+
+def lmh(**kw):
+    a = dict(y=P, w=P, rs=NULL, gbs=1, H=16, H_u=16, V=64, flags=0, logits=P)
+    a.update(kw)
+    return dst.lib().tail_lm_head(a["y"], a["w"], a["rs"], a["gbs"], a["H"], a["H_u"], a["V"],
+                                  a["flags"], a["logits"], None, 0, None)
+
+
+def test_lm_head_validation():
+    E = dst.ERR_INVALID_ARG
+    assert lmh(gbs=0) == E
+    assert lmh(V=0) == E
+    assert lmh(V=12) == dst.ERR_UNSUPPORTED                     # not a multiple of 8
+    assert lmh(w=NULL) == E
+    assert lmh(y=NULL) == E
+    assert lmh(logits=NULL) == E
+    assert lmh(w=ctypes.c_void_p(0x100008)) == E               # weight must be 16-byte aligned
+    assert lmh(logits=ctypes.c_void_p(0x100004)) == E
+    assert lmh(H_u=20) == E
+    assert lmh(flags=1 << 5) == E
+
+
+def tk(**kw):
+    a = dict(logits=P, gbs=2, V=4096, k=16, vals=P, idx=P, ws=P, ws_bytes=1 << 20)
+    a.update(kw)
+    return dst.lib().tail_topk(a["logits"], a["gbs"], a["V"], a["k"], a["vals"], a["idx"], a["ws"],
+                               a["ws_bytes"], None)
+
+
+def test_topk_validation():
+    E = dst.ERR_INVALID_ARG
+    assert tk(k=0) == E
+    assert tk(k=4097) == E                                      # k > V
+    assert tk(V=8192, k=dst.K_MAX + 1) == dst.ERR_UNSUPPORTED
+    assert tk(gbs=0) == E
+    assert tk(logits=NULL) == E
+    assert tk(vals=NULL) == E
+    assert tk(idx=NULL) == E
+    assert tk(V=4100) == dst.ERR_UNSUPPORTED
+    assert tk(ws=NULL) == dst.ERR_WORKSPACE
+    assert tk(ws=ctypes.c_void_p(0x100010)) == dst.ERR_WORKSPACE
+    # 16 groups of 256 columns per row: 2 rows * 16 * 4 bytes of group maxima, in
+    # one 256-byte aligned block
+    assert tk(ws_bytes=255) == dst.ERR_WORKSPACE
+    assert dst.workspace_size(2, 1, 1, 4096, 16, dst.EMIT_LOGITS) >= 256
+
+
+def smp(**kw):
+    a = dict(vals=P, idx=P, gbs=4, k=256, params=P, ncols=4, tokens=P)
+    a.update(kw)
+    return dst.lib().tail_sample(a["vals"], a["idx"], a["gbs"], a["k"], a["params"], a["ncols"],
+                                 a["tokens"], None)
+
+
+def test_sample_validation():
+    E = dst.ERR_INVALID_ARG
+    assert smp(ncols=2) == E
+    assert smp(ncols=5) == E
+    assert smp(k=0) == E
+    assert smp(gbs=0) == E
+    assert smp(params=NULL) == E
+    assert smp(tokens=NULL) == E
+    assert smp(k=dst.K_MAX + 1) == dst.ERR_UNSUPPORTED
+
+
+def fwd(**kw):
+    a = dict(hidden=P, dtype=dst.BF16, gamma=P, w=P, gbs=8, H=2880, H_u=2880, V=201088, k=256,
+             eps=1e-5, flags=dst.EMIT_LOGITS, params=P, ncols=4, logits=P, vals=P, idx=P, tokens=P,
+             ws=P, ws_bytes=1 << 40)
+    a.update(kw)
+    return dst.lib().tail_forward(a["hidden"], a["dtype"], a["gamma"], a["w"], a["gbs"], a["H"],
+                                  a["H_u"], a["V"], a["k"], a["eps"], a["flags"], a["params"],
+                                  a["ncols"], a["logits"], a["vals"], a["idx"], a["tokens"], a["ws"],
+                                  a["ws_bytes"], None)
+
+
+def test_forward_validation():
+    E = dst.ERR_INVALID_ARG
+    assert fwd(logits=NULL) == E                                # EMIT_LOGITS needs logits
+    assert fwd(params=P, tokens=NULL) == E
+    assert fwd(ncols=2) == E
+    assert fwd(vals=NULL) == E
+    assert fwd(idx=NULL) == E
+    assert fwd(w=NULL) == E
+    assert fwd(dtype=7) == E
+    assert fwd(k=257, V=256) == E
+    assert fwd(H=3072, H_u=2880, flags=dst.ZERO_PAD | 8) == E   # unknown flag bit
+    assert fwd(ws=NULL) == dst.ERR_WORKSPACE
+    need = dst.workspace_size(8, 2880, 2880, 201088, 256, dst.EMIT_LOGITS)
+    assert fwd(ws_bytes=need - 1) == dst.ERR_WORKSPACE
+    assert fwd(V=201090) == dst.ERR_UNSUPPORTED
+
+
+def test_workspace_size():
+    ws = dst.workspace_size
+    assert ws(0, 16, 16, 64, 4, 0) == 0
+    assert ws(1, 16, 16, 64, 65, 0) == 0
+    assert ws(1, 3072, 2881, 64, 4, dst.ZERO_PAD) == 0
+    base = ws(8, 2880, 2880, 201088, 256, dst.EMIT_LOGITS)
+    assert base % 256 == 0 and base > 0
+    # without emitted logits the workspace holds them: +gbs*V*4 bytes (rounded)
+    assert ws(8, 2880, 2880, 201088, 256, 0) >= base + 8 * 201088 * 4
+    prev = 0
+    for gbs in (1, 2, 8, 64, 256):
+        cur = ws(gbs, 2880, 2880, 201088, 256, 0)
+        assert cur > prev
+        prev = cur
