@@ -128,7 +128,7 @@ def rmsnorm(hidden, gamma, H_u=None, eps=1e-5, zero_pad=False, deferred=False, o
     return y, r
 
 
-def lm_head(y, w_t, H_u=None, zero_pad=False, row_scale=None, out=None):
+def lm_head(y, w_t, H_u=None, zero_pad=False, row_scale=None, out=None, ws=None):
     """tail_lm_head: logits [gbs,V] fp32 = row_scale * (y @ W)."""
     torch = _torch()
     dev = _dev(y)
@@ -136,8 +136,11 @@ def lm_head(y, w_t, H_u=None, zero_pad=False, row_scale=None, out=None):
     V = w_t.shape[1]
     H_u = H if H_u is None else H_u
     logits = out if out is not None else torch.empty((gbs, V), dtype=torch.float32, device=dev)
+    if ws is None:
+        n = workspace_size(gbs, H, H_u, V, 1, _flags(zero_pad, emit=True))
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     _call("tail_lm_head", _ptr(y), _ptr(_weight(w_t)), _ptr(row_scale), gbs, H, H_u, V,
-          _flags(zero_pad), _ptr(logits), None, 0, _stream(dev))
+          _flags(zero_pad), _ptr(logits), _ptr(ws), ws.numel(), _stream(dev))
     return logits
 
 

@@ -27,6 +27,15 @@ constexpr int kSlab = 512;  // columns per workgroup
 constexpr int kUnroll = 8;  // weight rows in flight per lane
 constexpr int kMaxNB = 8;   // batch rows per pass
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// The weight is streamed once and never reused: non-temporal loads keep it
+// from displacing useful lines and measurably raise the achieved bandwidth.
+__device__ inline uint4 load_stream(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -35,7 +44,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const float* __restrict_
                                                         const uint16_t* __restrict__ w,
                                                         const float* __restrict__ row_scale,
                                                         int H_u, int pad_s, int V,
-                                                        float* __restrict__ logits, int b0) {
+                                                        float* __restrict__ logits,
+                                                        uint32_t* __restrict__ gkey, int groups,
+                                                        int b0) {
   __shared__ float4 s_red[4][NB][kSlab / 4];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -63,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const float* __restrict_
     for (int j = 0; j < kUnroll; ++j) {
       hh[j] = h;
       wv[j] = make_uint4(0, 0, 0, 0);
-      if (u + j < u1 && act) wv[j] = *reinterpret_cast<const uint4*>(wcol + size_t(h) * V);
+      if (u + j < u1 && act) wv[j] = load_stream(wcol + size_t(h) * V);
       ++h;
       if (pad_s && ++gpos == pad_s - 1) {
         ++h;
@@ -107,40 +118,59 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const float* __restrict_
     __syncthreads();
   }
 
-  if (wave == 0 && act) {
+  if (wave == 0) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const float s = row_scale ? row_scale[b0 + b] : 1.0f;
-      float4* out = reinterpret_cast<float4*>(logits + size_t(b0 + b) * V + col);
-      out[0] = make_float4(acc[b][0] * s, acc[b][1] * s, acc[b][2] * s, acc[b][3] * s);
-      out[1] = make_float4(acc[b][4] * s, acc[b][5] * s, acc[b][6] * s, acc[b][7] * s);
+      float o[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[c] = acc[b][c] * s;
+      if (act) {
+        float4* out = reinterpret_cast<float4*>(logits + size_t(b0 + b) * V + col);
+        out[0] = make_float4(o[0], o[1], o[2], o[3]);
+        out[1] = make_float4(o[4], o[5], o[6], o[7]);
+      }
+      if (gkey) {  // maxima of the 64-column groups: 8 lanes each
+        uint32_t m = 0;
+        if (act) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) m = max(m, float_key(o[c]));
+        }
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+        const int g = blockIdx.x * (kSlab / kFusedGroup) + lane / 8;
+        if ((lane & 7) == 0 && g < groups) gkey[size_t(b0 + b) * groups + g] = m;
+      }
     }
   }
 }
 
 template <int NB>
 void launch_nb(dim3 grid, hipStream_t st, const float* y, int ldy, const uint16_t* w,
-               const float* rs, int H_u, int pad_s, int V, float* logits, int b0) {
+               const float* rs, int H_u, int pad_s, int V, float* logits, uint32_t* gkey,
+               int groups, int b0) {
   hipLaunchKernelGGL(gemv_kernel<NB>, grid, dim3(kThreads), 0, st, y, ldy, w, rs, H_u, pad_s, V,
-                     logits, b0);
+                     logits, gkey, groups, b0);
 }
 
 }  // namespace
 
 hipError_t launch_lm_head_gemv(const float* y, int ldy, const uint16_t* w, const float* row_scale,
-                               int gbs, int H_u, int pad_s, int V, float* logits, hipStream_t st) {
+                               int gbs, int H_u, int pad_s, int V, float* logits, uint32_t* gkey,
+                               hipStream_t st) {
   dim3 grid((V + kSlab - 1) / kSlab);
+  const int groups = (V + kFusedGroup - 1) / kFusedGroup;
   for (int b0 = 0; b0 < gbs; b0 += kMaxNB) {
     int nb = gbs - b0 < kMaxNB ? gbs - b0 : kMaxNB;
     switch (nb) {
-      case 1: launch_nb<1>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, b0); break;
-      case 2: launch_nb<2>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, b0); break;
-      case 3: launch_nb<3>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, b0); break;
-      case 4: launch_nb<4>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, b0); break;
-      case 5: launch_nb<5>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, b0); break;
-      case 6: launch_nb<6>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, b0); break;
-      case 7: launch_nb<7>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, b0); break;
-      default: launch_nb<8>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, b0); break;
+      case 1: launch_nb<1>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
+      case 2: launch_nb<2>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
+      case 3: launch_nb<3>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
+      case 4: launch_nb<4>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
+      case 5: launch_nb<5>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
+      case 6: launch_nb<6>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
+      case 7: launch_nb<7>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
+      default: launch_nb<8>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -2,13 +2,15 @@
 // parameters "gamma", "eps", "hidden_actual", "hidden_states",
 // "zero_interleaved_pad", "deferred_rms").
 //
-// One 256-thread workgroup per row.  The row is read once with coalesced
-// loads, widened exactly to fp32 (fp16 via the hardware conversion, bf16 by a
-// 16-bit shift), and its sum of squares is accumulated in fp64 in a fixed
-// order (per-thread strided partials, then a fixed butterfly and a fixed
-// cross-wave sum), so r is a correctly rounded fp32 of 1/sqrt(ms + eps) in
-// all but pathological cases and every row gives the same bytes alone or in
-// a batch.  Bytes moved per row: H * (dtype bytes + 4 for gamma + 4 for y).
+// One 256-thread workgroup per row.  Each thread owns lanes t, t+256, ...
+// of the row; up to 16 of them (H <= 4096) are loaded in one unrolled burst
+// so the row costs one memory latency, and stay in registers for the output
+// pass.  Longer rows are processed in bursts of 4096 lanes and re-read.  The
+// values are widened exactly to fp32 (fp16 by the hardware conversion, bf16
+// by a 16-bit shift); the sum of squares is accumulated in fp64 in a fixed
+// order (per-thread ascending lanes, a fixed butterfly, a fixed cross-wave
+// sum), so r = fp32(1/sqrt(ms + eps)) is the same for a row alone or in a
+// batch.  Bytes per row: H * (dtype bytes + 4 gamma + 4 output).
 #include "tail_internal.h"
 
 #include <hip/hip_fp16.h>
@@ -17,6 +19,8 @@ namespace tail {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPer = 16;  // lanes per thread per burst
+constexpr int kBurst = kThreads * kPer;
 
 template <int DT>
 __device__ inline float load_hidden(const void* p, size_t i) {
@@ -35,6 +39,18 @@ __device__ inline double wave_sum(double v) {
   return v;
 }
 
+__device__ inline bool is_pad(int h, int pad_s) { return pad_s && (h % pad_s == pad_s - 1); }
+
+template <int DT>
+__device__ inline void load_burst(const void* hidden, size_t base, int h0, int H, int pad_s, int tid,
+                                  float (&x)[kPer]) {
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int h = h0 + tid + i * kThreads;
+    x[i] = (h < H && !is_pad(h, pad_s)) ? load_hidden<DT>(hidden, base + h) : 0.0f;
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restrict__ hidden,
                                                            const float* __restrict__ gamma, int H,
@@ -46,32 +62,116 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restric
   const int tid = threadIdx.x;
   const size_t base = size_t(row) * H;
 
+  float x[kPer];
   double ss = 0.0;
-  for (int h = tid; h < H; h += kThreads) {
-    bool pad = pad_s && (h % pad_s == pad_s - 1);
-    if (!pad) {
-      double x = load_hidden<DT>(hidden, base + h);
-      ss = fma(x, x, ss);
-    }
+  for (int h0 = 0; h0 < H; h0 += kBurst) {
+    load_burst<DT>(hidden, base, h0, H, pad_s, tid, x);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) ss = fma(double(x[i]), double(x[i]), ss);
   }
   ss = wave_sum(ss);
   if ((tid & 63) == 0) s_part[tid >> 6] = ss;
   __syncthreads();
-  double tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
-  double ms = tot / double(H_u);
-  float r = float(1.0 / sqrt(ms + double(eps)));
+  const double tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+  const float r = float(1.0 / sqrt(tot / double(H_u) + double(eps)));
 
-  for (int h = tid; h < H; h += kThreads) {
-    bool pad = pad_s && (h % pad_s == pad_s - 1);
-    float out = 0.0f;
-    if (!pad) {
-      float x = load_hidden<DT>(hidden, base + h);
-      float g = gamma[h];
-      out = deferred ? x * g : (x * r) * g;
+  for (int h0 = 0; h0 < H; h0 += kBurst) {
+    if (H > kBurst) load_burst<DT>(hidden, base, h0, H, pad_s, tid, x);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int h = h0 + tid + i * kThreads;
+      if (h < H) {
+        float out = 0.0f;
+        if (!is_pad(h, pad_s)) {
+          const float g = gamma[h];
+          out = deferred ? x[i] * g : (x[i] * r) * g;
+        }
+        y[base + h] = out;
+      }
     }
-    y[base + h] = out;
   }
   if (tid == 0 && r_out) r_out[row] = r;
+}
+
+// ---------------------------------------------------------------------------
+// Activation producer for the matrix-core lm_head.  One workgroup per batch
+// row (rows gbs..rows_pad-1 are written as zeros).  K is the number of lanes
+// the contraction runs over (H_u when pad lanes are skipped, else H); the
+// mean square always divides by H_u.  The row's activation
+//   NORM:  y = x * gamma (deferred rms; r is written to r_out) or (x * r) * gamma
+//   !NORM: y = the given fp32 row
+// is taken over the real lanes only (compacted: unpadded index u), zero-padded
+// to Kp, and split into NT bf16 terms t_0 = bf16(y), t_1 = bf16(y - t_0),
+// t_2 = bf16(y - t_0 - t_1) (round to nearest even; each difference is exact
+// in fp32).  Inside each block of 32 lanes, unpadded lane 32 q + c is stored
+// at slot 32 q + p with c = 4 (p / 8 % 4) + (p % 4) + 16 (p % 8 / 4): the K
+// order of the matrix-core kernel's operands.
+__device__ inline uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ inline float bf16_val(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+__device__ inline int k_slot(int u) {
+  const int c = u & 31;
+  return (u & ~31) | (8 * ((c & 15) >> 2) + 4 * (c >> 4) + (c & 3));
+}
+
+template <int DT, int NT, bool NORM>
+__global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict__ src,
+                                                         const float* __restrict__ gamma, int H,
+                                                         int H_u, int K, int pad_s, FastDiv pdiv,
+                                                         float eps, int deferred, int gbs,
+                                                         int rows_pad, int Kp,
+                                                         uint16_t* __restrict__ act,
+                                                         float* __restrict__ r_out) {
+  __shared__ double s_part[kThreads / 64];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (row >= gbs) {
+    for (int i = tid; i < Kp; i += kThreads)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) act[(size_t(t) * rows_pad + row) * Kp + i] = 0;
+    return;
+  }
+  const size_t base = size_t(row) * H;
+  float r = 1.0f;
+  if constexpr (NORM) {
+    float x[kPer];
+    double ss = 0.0;
+    for (int h0 = 0; h0 < H; h0 += kBurst) {
+      load_burst<DT>(src, base, h0, H, pad_s, tid, x);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) ss = fma(double(x[i]), double(x[i]), ss);
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) s_part[tid >> 6] = ss;
+    __syncthreads();
+    const double tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+    r = float(1.0 / sqrt(tot / double(H_u) + double(eps)));
+    if (tid == 0 && r_out) r_out[row] = r;
+  }
+  for (int u = tid; u < Kp; u += kThreads) {
+    float y = 0.0f;
+    if (u < K) {
+      const int h = pad_s ? u + int(fastdiv(uint32_t(u), pdiv)) : u;
+      const float x = load_hidden<DT>(src, base + h);
+      if constexpr (NORM) {
+        const float g = gamma[h];
+        y = deferred ? x * g : (x * r) * g;
+      } else {
+        y = x;
+      }
+    }
+    const int slot = k_slot(u);
+    float rem = y;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint16_t b = bf16_rne(rem);
+      act[(size_t(t) * rows_pad + row) * Kp + slot] = b;
+      rem = rem - bf16_val(b);
+    }
+  }
 }
 
 }  // namespace
@@ -94,6 +194,33 @@ hipError_t launch_rmsnorm(const void* hidden, int dtype, const float* gamma, int
                          int(deferred), y, r);
       break;
   }
+  return hipGetLastError();
+}
+
+}  // namespace tail
+
+namespace tail {
+
+hipError_t launch_split(const void* src, int dtype, bool norm, const float* gamma, int gbs, int H,
+                        int H_u, int K, int pad_s, float eps, bool deferred, int nt, int rows_pad,
+                        int Kp, uint16_t* act, float* r, hipStream_t st) {
+  const FastDiv pdiv = make_fastdiv(pad_s > 1 ? uint32_t(pad_s - 1) : 1u);
+  dim3 grid(rows_pad), block(kThreads);
+#define TAIL_SPLIT(DT, NT, NORM)                                                              \
+  hipLaunchKernelGGL((split_kernel<DT, NT, NORM>), grid, block, 0, st, src, gamma, H, H_u, K, \
+                     pad_s, pdiv, eps, int(deferred), gbs, rows_pad, Kp, act, r)
+  if (!norm) {
+    if (nt == 3) TAIL_SPLIT(0, 3, false); else TAIL_SPLIT(0, 2, false);
+  } else if (nt == 3) {
+    if (dtype == 0) TAIL_SPLIT(0, 3, true);
+    else if (dtype == 1) TAIL_SPLIT(1, 3, true);
+    else TAIL_SPLIT(2, 3, true);
+  } else {
+    if (dtype == 0) TAIL_SPLIT(0, 2, true);
+    else if (dtype == 1) TAIL_SPLIT(1, 2, true);
+    else TAIL_SPLIT(2, 2, true);
+  }
+#undef TAIL_SPLIT
   return hipGetLastError();
 }
 

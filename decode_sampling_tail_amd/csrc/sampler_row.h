@@ -1,0 +1,95 @@
+// One wave samples one row from its k candidates (GPT-OSS tail API page,
+// parameter "sampling_params": per-row [top_k, top_p, temperature] plus the
+// optional inverse-transform draw u, 0.5 when absent; temperature 0 is the
+// greedy argmax of the GK decode design).  Shared by the standalone sampler
+// kernel and the fused top-k + sampler kernel.
+//
+// Lane l owns candidates l*P .. l*P+P-1 (P = ceil(k/64)), so candidate order
+// is lane order.  The softmax numerators, the running sums and both cut
+// comparisons are evaluated in fp64:
+//
+//   kk = trunc(top_k), or k when top_k is not in [1, k+1)
+//   T <= 0 (or NaN): token = idx[0]
+//   e_i = exp((v_i - v_0) / T), i < kk;   S_i = e_0 + ... + e_i
+//   m = 1 + min{i < kk : S_i >= top_p * S_{kk-1}}   (kk if none)
+//   j = min{i < m : S_i > u * S_{m-1}}              (m-1 if none)
+//   token = idx[j]
+#pragma once
+
+#include <climits>
+
+#include "tail_internal.h"
+
+namespace tail {
+
+__device__ inline int wave_min_i32(int v) {
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// vals / ix: the row's candidates in descending order (global or LDS memory).
+// Returns the token on every lane.
+template <int P, typename VP, typename IP>
+__device__ inline int32_t sample_row_wave(VP vals, IP ix, int k, float top_k, float top_p,
+                                          float temp, float u, int lane) {
+  const int kk = (top_k >= 1.0f && top_k < float(k) + 1.0f) ? int(top_k) : k;
+  if (!(temp > 0.0f)) return ix[0];
+
+  const double v0 = vals[0], T = temp;
+  double S[P];
+  double run = 0.0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int i = lane * P + j;
+    const double e = i < kk ? exp((double(vals[i]) - v0) / T) : 0.0;
+    run += e;
+    S[j] = run;
+  }
+  double incl = run;  // inclusive prefix of the lane totals, in lane order
+  for (int off = 1; off < 64; off <<= 1) {
+    const double t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  const double excl = incl - run;
+#pragma unroll
+  for (int j = 0; j < P; ++j) S[j] += excl;
+
+  auto S_at = [&](int i) {  // S_i broadcast from its owner lane
+    double mine = 0.0;
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+      if (j == i % P) mine = S[j];
+    return __shfl(mine, i / P, 64);
+  };
+
+  const double pthr = double(top_p) * S_at(kk - 1);
+  int first = INT_MAX;
+#pragma unroll
+  for (int j = P - 1; j >= 0; --j) {
+    const int i = lane * P + j;
+    if (i < kk && S[j] >= pthr) first = i;
+  }
+  first = wave_min_i32(first);
+  const int m = first == INT_MAX ? kk : first + 1;
+
+  const double uthr = double(u) * S_at(m - 1);
+  first = INT_MAX;
+#pragma unroll
+  for (int j = P - 1; j >= 0; --j) {
+    const int i = lane * P + j;
+    if (i < m && S[j] > uthr) first = i;
+  }
+  first = wave_min_i32(first);
+  return ix[first == INT_MAX ? m - 1 : first];
+}
+
+// Row parameters from a [gbs, ncols] fp32 array (u = 0.5 without a 4th column).
+struct RowParams {
+  float top_k, top_p, temp, u;
+};
+__device__ inline RowParams load_params(const float* params, int ncols, int row) {
+  const float* p = params + size_t(row) * ncols;
+  return RowParams{p[0], p[1], p[2], ncols == 4 ? p[3] : 0.5f};
+}
+
+}  // namespace tail

@@ -46,11 +46,26 @@ int check_k(int V, int k) {
   return TAIL_OK;
 }
 
+// Geometry of the matrix-core path's split activations: [nt][rows_pad][Kp] bf16.
+struct SplitGeom {
+  int K, Kp, rows_pad, nt;
+  size_t bytes;
+};
+SplitGeom split_geom(int gbs, int H, int H_u, int pad_s) {
+  SplitGeom g;
+  g.K = pad_s ? H_u : H;
+  g.Kp = (g.K + tail::kKStep - 1) / tail::kKStep * tail::kKStep;
+  g.rows_pad = (gbs + 15) / 16 * 16;
+  g.nt = tail::mfma_terms(gbs);
+  g.bytes = gbs > tail::kGemvMaxBatch ? size_t(g.nt) * g.rows_pad * g.Kp * 2 : 0;
+  return g;
+}
+
 struct FwdLayout {
-  size_t y, r, logits, gkey, total;
+  size_t y, r, act, logits, gkey, total;
 };
 
-FwdLayout forward_layout(int gbs, int H, int V, int k, unsigned flags) {
+FwdLayout forward_layout(int gbs, int H, int H_u, int pad_s, int V, int k, unsigned flags) {
   tail::TopkGeom g;
   tail::topk_geometry(V, k, &g);
   FwdLayout L;
@@ -59,6 +74,8 @@ FwdLayout forward_layout(int gbs, int H, int V, int k, unsigned flags) {
   off = align256(off + size_t(gbs) * H * 4);
   L.r = off;
   off = align256(off + size_t(gbs) * 4);
+  L.act = off;
+  off = align256(off + split_geom(gbs, H, H_u, pad_s).bytes);
   L.logits = off;
   if (!(flags & TAIL_EMIT_LOGITS)) off = align256(off + size_t(gbs) * V * 4);
   L.gkey = off;
@@ -97,9 +114,12 @@ TAIL_API const char* tail_status_string(int status) {
 TAIL_API size_t tail_workspace_size(int gbs, int H, int H_u, int V, int k, unsigned flags) {
   if (check_shape(gbs, H, H_u) || check_vocab(V) || check_k(V, k)) return 0;
   if (pad_stride(H, H_u, flags) < 0) return 0;
-  size_t fwd = forward_layout(gbs, H, V, k, flags).total;
+  const int ps = pad_stride(H, H_u, flags);
+  size_t fwd = forward_layout(gbs, H, H_u, ps, V, k, flags).total;
   size_t tk = topk_ws_bytes(gbs, V, k);
-  return fwd > tk ? fwd : tk;
+  size_t lm = align256(split_geom(gbs, H, H_u, ps).bytes);
+  size_t m = fwd > tk ? fwd : tk;
+  return m > lm ? m : lm;
 }
 
 TAIL_API int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int H,
@@ -132,12 +152,19 @@ TAIL_API int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_
   if (!aligned(y, 4) || !aligned(w_t, 16) || !aligned(logits, 16) ||
       (row_scale && !aligned(row_scale, 4)))
     return TAIL_ERR_INVALID_ARG;
-  (void)ws;
-  (void)ws_bytes;  // this path needs no workspace
-  // without pad skipping every lane of the hidden is used
-  int H_used = ps ? H_u : H;
-  return hip_status(tail::launch_lm_head_gemv(y, H, w_t, row_scale, gbs, H_used, ps, V, logits,
-                                              (hipStream_t)stream));
+  const SplitGeom sg = split_geom(gbs, H, H_u, ps);
+  if (int s = check_ws(ws, ws_bytes, sg.bytes)) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (gbs <= tail::kGemvMaxBatch)
+    return hip_status(tail::launch_lm_head_gemv(y, H, w_t, row_scale, gbs, sg.K, ps, V, logits,
+                                                nullptr, st));
+  uint16_t* act = (uint16_t*)ws;
+  hipError_t e = tail::launch_split(y, TAIL_F32, false, nullptr, gbs, H, H_u, sg.K, ps, 0.0f, false,
+                                    sg.nt, sg.rows_pad, sg.Kp, act, nullptr, st);
+  if (e == hipSuccess)
+    e = tail::launch_lm_head_mfma(act, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps, row_scale, gbs, logits,
+                                  nullptr, st);
+  return hip_status(e);
 }
 
 TAIL_API int tail_topk(const float* logits, int gbs, int V, int k, float* vals, int32_t* idx,
@@ -188,23 +215,39 @@ TAIL_API int tail_forward(const void* hidden, int dtype, const float* gamma, con
       !aligned(vals, 4) || !aligned(idx, 4) || (emit && !aligned(logits, 16)) ||
       (params && (!aligned(params, 4) || !aligned(tokens, 4))))
     return TAIL_ERR_INVALID_ARG;
-  FwdLayout L = forward_layout(gbs, H, V, k, flags);
+  FwdLayout L = forward_layout(gbs, H, H_u, ps, V, k, flags);
   if (int s = check_ws(ws, ws_bytes, L.total)) return s;
 
   hipStream_t st = (hipStream_t)stream;
   char* base = (char*)ws;
   float* y = (float*)(base + L.y);
   float* r = (float*)(base + L.r);
+  uint16_t* act = (uint16_t*)(base + L.act);
   float* lg = emit ? logits : (float*)(base + L.logits);
   uint32_t* gk = (uint32_t*)(base + L.gkey);
-  bool deferred = flags & TAIL_DEFERRED_RMS;
+  const bool deferred = flags & TAIL_DEFERRED_RMS;
   tail::TopkGeom g;
   tail::topk_geometry(V, k, &g);
-  hipError_t e = tail::launch_rmsnorm(hidden, dtype, gamma, gbs, H, H_u, ps, eps, deferred, y, r, st);
+  const SplitGeom sg = split_geom(gbs, H, H_u, ps);
+  // group maxima come from the lm_head epilogue when the top-k groups are its
+  // 64-column groups; otherwise from a separate pass over the logits
+  const bool fused_groups = g.gs == tail::kFusedGroup;
+  uint32_t* gk_fused = fused_groups ? gk : nullptr;
+  hipError_t e;
+  if (gbs <= tail::kGemvMaxBatch) {  // RMSNorm -> weight-streaming lm_head
+    e = tail::launch_rmsnorm(hidden, dtype, gamma, gbs, H, H_u, ps, eps, deferred, y, r, st);
+    if (e == hipSuccess)
+      e = tail::launch_lm_head_gemv(y, H, w_t, deferred ? r : nullptr, gbs, sg.K, ps, V, lg,
+                                    gk_fused, st);
+  } else {  // RMSNorm + bf16 split -> matrix-core lm_head
+    e = tail::launch_split(hidden, dtype, true, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, sg.nt,
+                           sg.rows_pad, sg.Kp, act, r, st);
+    if (e == hipSuccess)
+      e = tail::launch_lm_head_mfma(act, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
+                                    deferred ? r : nullptr, gbs, lg, gk_fused, st);
+  }
+  if (e == hipSuccess && !fused_groups) e = tail::launch_group_max(lg, gbs, V, g, gk, st);
   if (e == hipSuccess)
-    e = tail::launch_lm_head_gemv(y, H, w_t, deferred ? r : nullptr, gbs, ps ? H_u : H, ps, V, lg, st);
-  if (e == hipSuccess) e = tail::launch_topk(lg, gbs, V, k, g, gk, vals, idx, st);
-  if (e == hipSuccess && params)
-    e = tail::launch_sample(vals, idx, gbs, k, params, ncols, tokens, st);
+    e = tail::launch_select(lg, gbs, V, k, g, gk, vals, idx, params, ncols, tokens, st);
   return hip_status(e);
 }

@@ -15,6 +15,29 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_
 // with one pad lane (s = 0: no padding).
 __host__ __device__ inline int phys_lane(int u, int s) { return s ? u + u / (s - 1) : u; }
 
+// Exact unsigned division by a run-time constant d >= 1 for n < 2^31
+// (multiply-high and shift, Granlund & Montgomery, "Division by invariant
+// integers using multiplication", PLDI 1994, section 4):
+// q = (mulhi(n, mul) + n) >> shift with shift = ceil(log2 d) and
+// mul = floor(2^32 * (2^shift - d) / d) + 1.
+struct FastDiv {
+  uint32_t mul, shift;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t shift = 0;
+  while ((uint64_t(1) << shift) < d) ++shift;
+  uint64_t mul = ((uint64_t(1) << 32) * ((uint64_t(1) << shift) - d)) / d + 1;
+  return FastDiv{uint32_t(mul), shift};
+}
+__host__ __device__ inline uint32_t fastdiv(uint32_t n, FastDiv f) {
+#ifdef __HIP_DEVICE_COMPILE__
+  const uint32_t hi = __umulhi(n, f.mul);
+#else
+  const uint32_t hi = uint32_t((uint64_t(n) * f.mul) >> 32);
+#endif
+  return (hi + n) >> f.shift;
+}
+
 // Order-preserving key of a float: larger float <=> larger unsigned key.
 // -0.0 is canonicalized to +0.0 so the two compare equal.
 __device__ inline uint32_t float_key(float f) {
@@ -28,12 +51,13 @@ __device__ inline uint32_t float_key(float f) {
 // maximum bounds the k-th largest logit from below, and at most
 // kMaxGroups of them so the group maxima of one row fit in LDS.
 constexpr int kMaxGroups = 8192;
+constexpr int kFusedGroup = 64;  // group size the lm_head epilogues emit maxima for
 struct TopkGeom {
   int gs;      // group size (columns)
   int groups;  // ceil(V / gs)
 };
 inline bool topk_geometry(int V, int k, TopkGeom* g) {
-  int gs = 256;
+  int gs = kFusedGroup;
   while (gs > 1 && (V + gs - 1) / gs < k) gs >>= 1;
   while ((V + gs - 1) / gs > kMaxGroups) gs <<= 1;
   g->gs = gs;
@@ -46,8 +70,35 @@ inline bool topk_geometry(int V, int k, TopkGeom* g) {
 hipError_t launch_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int H, int H_u,
                           int pad_s, float eps, bool deferred, float* y, float* r, hipStream_t st);
 
+// gkey (may be NULL): per row, the largest order-preserving key of each group
+// of kFusedGroup columns, [gbs, ceil(V / kFusedGroup)].
 hipError_t launch_lm_head_gemv(const float* y, int ldy, const uint16_t* w, const float* row_scale,
-                               int gbs, int H_u, int pad_s, int V, float* logits, hipStream_t st);
+                               int gbs, int H_u, int pad_s, int V, float* logits, uint32_t* gkey,
+                               hipStream_t st);
+
+// Batches above this size run the lm_head on the matrix cores.
+constexpr int kGemvMaxBatch = 4;
+constexpr int kKStep = 64;  // K granularity of the matrix-core path
+int mfma_terms(int gbs);    // bf16 terms per activation for that batch size
+
+// Split (and, with norm, RMS-normalize) activations for the matrix-core path:
+// act [nt][rows_pad][Kp] bf16 bits over the K contraction lanes; r [gbs]
+// (norm only, may be NULL).
+hipError_t launch_split(const void* src, int dtype, bool norm, const float* gamma, int gbs, int H,
+                        int H_u, int K, int pad_s, float eps, bool deferred, int nt, int rows_pad,
+                        int Kp, uint16_t* act, float* r, hipStream_t st);
+
+hipError_t launch_lm_head_mfma(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V,
+                               int H_u, int pad_s, const float* row_scale, int gbs, float* logits,
+                               uint32_t* gkey, hipStream_t st);
+
+hipError_t launch_group_max(const float* logits, int gbs, int V, const TopkGeom& geom,
+                            uint32_t* gkey, hipStream_t st);
+
+// params NULL: no sampling (ncols and tokens unused)
+hipError_t launch_select(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
+                         const uint32_t* gkey, float* vals, int32_t* idx, const float* params,
+                         int ncols, int32_t* tokens, hipStream_t st);
 
 hipError_t launch_topk(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
                        uint32_t* gkey_ws, float* vals, int32_t* idx, hipStream_t st);

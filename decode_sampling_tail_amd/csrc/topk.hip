@@ -1,34 +1,34 @@
 // Global top-k of every logit row over the full vocabulary (GPT-OSS tail API
 // page: Background -- the global top-k is computed locally over the full
-// vocabulary -- and parameter "k").
+// vocabulary -- and parameter "k"), optionally followed by the row's sampler.
 //
-// Two kernels:
+// Input: the logits and, per row, the largest order-preserving key of every
+// group of gs consecutive columns (gs a power of two with at least k groups).
+// The lm_head kernels write those group maxima in their epilogue; for other
+// inputs group_max_kernel computes them in one pass over the logits.
 //
-// 1. group_max_kernel: the row is cut into groups of gs columns (gs a power of
-//    two chosen so there are at least k groups); one wave reduces one group to
-//    the largest order-preserving key of its values.  This is the only pass
-//    over the whole logit row (V * 4 bytes per row).
+// select_kernel, one 1024-thread workgroup per row:
+//  a. t0 = the k-th largest group maximum (radix select, 8-bit digits).  At
+//     least k groups have a maximum >= t0 and each maximum is an element, so
+//     every top-k member is >= t0, and only groups whose maximum is >= t0 can
+//     hold one.
+//  b. Those groups are scanned (loads batched four deep per thread) and every
+//     element >= t0 is appended to an LDS list as the composite key
+//     (value key << 32) | ~index: larger value first, lower index first.
+//  c. Lists longer than 2k are cut to the k-th largest value v* (radix select)
+//     and, when ties at v* would still leave more than 2k, to the lowest
+//     indices among the elements equal to v* (radix select on ~index).
+//  d. Each survivor's rank is the number of survivors with a larger composite
+//     key; ranks below k are written out (and kept in LDS for the sampler).
+//  e. More than kCap elements >= t0 (massive ties): the same two cuts are
+//     found by radix passes that re-read the candidate groups, then only the
+//     k winners are collected.  Exact for any input, slow only for such rows.
+//  f. With sampling parameters, wave 0 samples the row from the sorted list.
 //
-// 2. select_kernel: one 1024-thread workgroup per row.
-//    a. t0 = the k-th largest group maximum (binary search on the key, counts
-//       over LDS).  At least k groups have a maximum >= t0 and each such
-//       maximum is an element, so at least k elements are >= t0: every member
-//       of the top-k is >= t0, and only groups whose maximum is >= t0 can hold
-//       one.  For Gaussian-like rows this leaves a few hundred candidates.
-//    b. The waves scan only those groups and append every (key, index) with
-//       key >= t0 to an LDS list (wave-aggregated atomic slot allocation).
-//    c. Candidates are ranked by the composite 64-bit key
-//       (value key << 32) | ~index, so larger value first and, for equal
-//       values, lower index first; rank < k is written out.  Long lists are
-//       first pruned to the keys >= the k-th largest value key.
-//    d. If more than kCap candidates pass (massive ties), the exact k-th
-//       largest value v* and, if needed, the index cut among the elements
-//       equal to v* are found by counting passes over the candidate groups,
-//       and only the k winners are collected.  Slow, but exact for any input.
-//
-// Values are copied from the logits themselves, so -0.0 keeps its sign while
-// comparing equal to +0.0.
-#include "tail_internal.h"
+// Values are copied from the logits, so -0.0 keeps its sign while ranking
+// equal to +0.0.
+#include "sampler_row.h"
+#include "../../include/tail.h"
 
 namespace tail {
 namespace {
@@ -36,19 +36,13 @@ namespace {
 constexpr int kGmThreads = 256;
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kCap = 4096;                       // LDS candidate capacity
-constexpr int kPerThread = kCap / kSelThreads;  // candidates per thread in registers
+constexpr int kCap = 4096;                        // LDS candidate capacity
+constexpr int kPerThread = kCap / kSelThreads;    // candidates per thread in registers
+constexpr int kGPer = kMaxGroups / kSelThreads;   // group keys per thread in registers
+constexpr int kBatch = 4;                         // float4 loads in flight per thread
 
 __device__ inline uint32_t wave_max_u32(uint32_t v) {
   for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-  return v;
-}
-__device__ inline uint32_t wave_min_u32(uint32_t v) {
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off, 64));
-  return v;
-}
-__device__ inline uint32_t wave_sum_u32(uint32_t v) {
-  for (int off = 32; off >= 1; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, 64);
   return v;
 }
 
@@ -77,202 +71,240 @@ __global__ __launch_bounds__(kGmThreads) void group_max_kernel(const float* __re
 }
 
 struct SelShared {
-  uint32_t g[kMaxGroups];  // group maximum keys of the row
-  uint64_t c[kCap];        // candidate composite keys
-  uint32_t red[2][kSelWaves];
-  uint32_t cnt;
-};
-
-// Block-wide reductions; every thread gets the result.  Two alternating
-// buffers make one barrier per call enough.
-struct Block {
-  SelShared& s;
-  int wave, lane, parity;
-  __device__ uint32_t sum(uint32_t v) {
-    v = wave_sum_u32(v);
-    if (lane == 0) s.red[parity][wave] = v;
-    __syncthreads();
-    uint32_t t = 0;
-#pragma unroll
-    for (int i = 0; i < kSelWaves; ++i) t += s.red[parity][i];
-    parity ^= 1;
-    return t;
-  }
-  __device__ uint32_t maxv(uint32_t v) {
-    v = wave_max_u32(v);
-    if (lane == 0) s.red[parity][wave] = v;
-    __syncthreads();
-    uint32_t t = 0;
-#pragma unroll
-    for (int i = 0; i < kSelWaves; ++i) t = max(t, s.red[parity][i]);
-    parity ^= 1;
-    return t;
-  }
-  __device__ uint32_t minv(uint32_t v) {
-    v = wave_min_u32(v);
-    if (lane == 0) s.red[parity][wave] = v;
-    __syncthreads();
-    uint32_t t = 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = 0; i < kSelWaves; ++i) t = min(t, s.red[parity][i]);
-    parity ^= 1;
-    return t;
-  }
+  uint32_t act[kMaxGroups];  // candidate groups of the row
+  uint64_t c[kCap];          // candidate composite keys
+  float top_v[TAIL_K_MAX];   // the sorted result, for the sampler
+  int32_t top_i[TAIL_K_MAX];
+  uint32_t hist[256];
+  uint32_t bc[4];
+  uint32_t cnt, nact;
 };
 
 __device__ inline uint64_t composite(uint32_t key, int e) {
   return (uint64_t(key) << 32) | uint64_t(~uint32_t(e));
 }
 
-// Append the lanes' (key, e) where pred holds; slots past kCap are counted
-// but not stored.
+// Block-wide radix select: the k-th largest (k >= 1) 32-bit key among those
+// visit(f) enumerates (f(key) once per key of the calling thread; every
+// thread calls visit).  Returns the key; *above = keys strictly greater,
+// *equal = keys equal to it.  The visited set must hold at least k keys.
+template <typename Visit>
+__device__ uint32_t radix_kth(SelShared& s, int tid, uint32_t k, Visit&& visit, uint32_t* above,
+                              uint32_t* equal) {
+  uint32_t prefix = 0, need = k, eq = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    if (tid < 256) s.hist[tid] = 0;
+    __syncthreads();
+    visit([&](uint32_t key) {
+      if ((key & hmask) == prefix) atomicAdd(&s.hist[(key >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    if (tid < 64) {  // wave 0: bins in descending digit order, lane l holds 255-4l .. 252-4l
+      uint32_t c[4], loc = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = s.hist[255 - 4 * tid - j];
+        loc += c[j];
+      }
+      uint32_t incl = loc;
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = (uint32_t)__shfl_up((int)incl, off, 64);
+        if (tid >= off) incl += t;
+      }
+      uint32_t run = incl - loc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (run < need && run + c[j] >= need) {
+          s.bc[0] = 255 - 4 * tid - j;
+          s.bc[1] = need - run;
+          s.bc[2] = c[j];
+        }
+        run += c[j];
+      }
+    }
+    __syncthreads();
+    prefix |= s.bc[0] << shift;
+    need = s.bc[1];
+    eq = s.bc[2];
+  }
+  *above = k - need;
+  *equal = eq;
+  return prefix;
+}
+
+// Append (key, e) of the lanes where pred holds; slots past kCap are counted
+// but not stored.  Must be called by all lanes of the wave.
 __device__ inline void wave_append(SelShared& s, bool pred, uint32_t key, int e, int lane) {
-  uint64_t mask = __ballot(pred);
+  const uint64_t mask = __ballot(pred);
   if (mask == 0) return;
   uint32_t base = 0;
   if (lane == 0) base = atomicAdd(&s.cnt, (uint32_t)__popcll(mask));
-  base = __shfl((int)base, 0, 64);
+  base = (uint32_t)__shfl((int)base, 0, 64);
   if (pred) {
-    uint32_t pos = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+    const uint32_t pos = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
     if (pos < kCap) s.c[pos] = composite(key, e);
   }
 }
 
-// Predicate of a candidate: key > kv, or key == kv and index < ilim.
-__device__ inline bool wins(uint32_t key, int e, uint32_t kv, int ilim) {
-  return key > kv || (key == kv && e < ilim);
-}
-
-// Visit every element of every group whose maximum is >= t0 (the only groups
-// that can hold a top-k member).  Wave w takes groups w, w + 16, ...; each
-// lane handles four consecutive columns per 256-column chunk.
+// Visit every element of the candidate groups, kBatch float4 loads in flight
+// per thread.  f(in, key, e) is called by all lanes of a wave the same number
+// of times (out-of-range slots have in == false).
 template <typename F>
-__device__ inline void for_candidate_groups(const SelShared& s, const float* row, int V, int gs,
-                                            int groups, uint32_t t0, int wave, int lane, F&& f) {
-  for (int g = wave; g < groups; g += kSelWaves) {
-    if (s.g[g] < t0) continue;
-    const int start = g * gs;
-    const int n = min(gs, V - start);
-    if (gs >= 4) {
-      for (int i0 = 0; i0 < n; i0 += 256) {
-        const int e0 = start + i0 + lane * 4;
-        const bool in = i0 + lane * 4 < n;
-        float4 v = in ? *reinterpret_cast<const float4*>(row + e0) : make_float4(0, 0, 0, 0);
-        f(in, float_key(v.x), e0);
-        f(in, float_key(v.y), e0 + 1);
-        f(in, float_key(v.z), e0 + 2);
-        f(in, float_key(v.w), e0 + 3);
+__device__ inline void for_candidates(const SelShared& s, const float* row, int V, int gs, int nact,
+                                      int tid, F&& f) {
+  const int wave_first = tid & ~63;
+  if (gs >= 4) {
+    const int per = gs >> 2;  // float4 items per group (a power of two)
+    const int lg = __ffs(per) - 1;
+    const int total = nact * per;
+    for (int w0 = wave_first; w0 < total; w0 += kBatch * kSelThreads) {
+      const int f0 = w0 + (tid & 63);
+      float4 v[kBatch];
+      int e[kBatch];
+      bool in[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int fi = f0 + u * kSelThreads;
+        in[u] = false;
+        e[u] = 0;
+        if (fi < total) {
+          e[u] = int(s.act[fi >> lg]) * gs + (fi & (per - 1)) * 4;
+          in[u] = e[u] < V;
+        }
+        v[u] = in[u] ? *reinterpret_cast<const float4*>(row + e[u]) : make_float4(0, 0, 0, 0);
       }
-    } else {
-      const bool in = lane < n;
-      f(in, in ? float_key(row[start + lane]) : 0u, start + lane);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        f(in[u], float_key(v[u].x), e[u]);
+        f(in[u], float_key(v[u].y), e[u] + 1);
+        f(in[u], float_key(v[u].z), e[u] + 2);
+        f(in[u], float_key(v[u].w), e[u] + 3);
+      }
+    }
+  } else {
+    const int total = nact * gs;
+    for (int w0 = wave_first; w0 < total; w0 += kSelThreads) {
+      const int fi = w0 + (tid & 63);
+      int e = 0;
+      bool in = false;
+      if (fi < total) {
+        e = int(s.act[fi / gs]) * gs + fi % gs;
+        in = e < V;
+      }
+      f(in, in ? float_key(row[e]) : 0u, e);
     }
   }
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ logits,
-                                                             int V, int gs, int groups, int k,
-                                                             const uint32_t* __restrict__ gkey,
-                                                             float* __restrict__ vals,
-                                                             int32_t* __restrict__ idx) {
+template <int P>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const float* __restrict__ logits, int V, int gs, int groups, int k,
+    const uint32_t* __restrict__ gkey, float* __restrict__ vals, int32_t* __restrict__ idx,
+    const float* __restrict__ params, int ncols, int32_t* __restrict__ tokens) {
   __shared__ SelShared s;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int row_id = blockIdx.x;
   const float* row = logits + size_t(row_id) * V;
-  Block blk{s, wave, lane, 0};
+  uint32_t above, equal;
 
-  // a. group maxima -> t0, the k-th largest of them
-  uint32_t lo_l = 0xFFFFFFFFu, hi_l = 0;
-  for (int g = tid; g < groups; g += kSelThreads) {
-    uint32_t v = gkey[size_t(row_id) * groups + g];
-    s.g[g] = v;
-    lo_l = min(lo_l, v);
-    hi_l = max(hi_l, v);
+  // a. t0 = k-th largest group maximum
+  uint32_t gk[kGPer];
+#pragma unroll
+  for (int j = 0; j < kGPer; ++j) {
+    const int g = tid + j * kSelThreads;
+    gk[j] = g < groups ? gkey[size_t(row_id) * groups + g] : 0u;
   }
-  if (tid == 0) s.cnt = 0;
-  uint64_t lo = blk.minv(lo_l);
-  uint64_t hi = uint64_t(blk.maxv(hi_l)) + 1;
-  while (hi - lo > 1) {  // count(>= lo) >= k > count(>= hi)
-    uint64_t mid = (lo + hi) >> 1;
-    uint32_t c = 0;
-    for (int g = tid; g < groups; g += kSelThreads) c += s.g[g] >= mid;
-    if (blk.sum(c) >= uint32_t(k)) lo = mid; else hi = mid;
-  }
-  const uint32_t t0 = uint32_t(lo);
+  if (tid == 0) s.cnt = s.nact = 0;
+  const uint32_t t0 = radix_kth(s, tid, uint32_t(k), [&](auto&& f) {
+#pragma unroll
+    for (int j = 0; j < kGPer; ++j)
+      if (tid + j * kSelThreads < groups) f(gk[j]);
+  }, &above, &equal);
 
-  // b. collect every element >= t0
-  uint32_t kv = t0;
-  int ilim = V;
-  for_candidate_groups(s, row, V, gs, groups, t0, wave, lane,
-                       [&](bool in, uint32_t key, int e) { wave_append(s, in && key >= t0, key, e, lane); });
+  // list the candidate groups
+#pragma unroll
+  for (int j = 0; j < kGPer; ++j) {
+    const bool a = tid + j * kSelThreads < groups && gk[j] >= t0;
+    const uint64_t m = __ballot(a);
+    if (m) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&s.nact, (uint32_t)__popcll(m));
+      base = (uint32_t)__shfl((int)base, 0, 64);
+      if (a) s.act[base + __popcll(m & ((1ull << lane) - 1ull))] = uint32_t(tid + j * kSelThreads);
+    }
+  }
+  __syncthreads();
+  const int nact = int(s.nact);
+
+  // b. every element >= t0
+  for_candidates(s, row, V, gs, nact, tid,
+                 [&](bool in, uint32_t key, int e) { wave_append(s, in && key >= t0, key, e, lane); });
   __syncthreads();
   uint32_t n = s.cnt;
 
-  // d. too many candidates: find the exact cut by counting passes
+  // e. too many: find the cut by radix passes over the candidate groups
   if (n > uint32_t(kCap)) {
-    auto count = [&](uint32_t kv_, int ilim_) {
-      uint32_t c = 0;
-      for_candidate_groups(s, row, V, gs, groups, t0, wave, lane,
-                           [&](bool in, uint32_t key, int e) { c += in && wins(key, e, kv_, ilim_); });
-      return blk.sum(c);
+    auto visit_all = [&](auto&& f) {
+      for_candidates(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int) {
+        if (in && key >= t0) f(key);
+      });
     };
-    uint64_t vlo = t0, vhi = hi;  // count(>= vlo) >= k > count(>= vhi)
-    while (vhi - vlo > 1) {
-      uint64_t mid = (vlo + vhi) >> 1;
-      if (count(uint32_t(mid), V) >= uint32_t(k)) vlo = mid; else vhi = mid;
-    }
-    kv = uint32_t(vlo);
-    if (count(kv, V) > uint32_t(kCap)) {  // ties at v*: keep the lowest indices
-      int ilo = 0, ihi = V;               // count(kv, ilo) < k <= count(kv, ihi)
-      while (ihi - ilo > 1) {
-        int mid = (ilo + ihi) >> 1;
-        if (count(kv, mid) >= uint32_t(k)) ihi = mid; else ilo = mid;
-      }
-      ilim = ihi;
+    const uint32_t vstar = radix_kth(s, tid, uint32_t(k), visit_all, &above, &equal);
+    int ecut = V;  // keep key > v*, and key == v* with index <= ecut
+    if (above + equal > uint32_t(kCap)) {
+      uint32_t a2, e2;
+      const uint32_t nk = radix_kth(s, tid, uint32_t(k) - above, [&](auto&& f) {
+        for_candidates(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int e) {
+          if (in && key == vstar) f(~uint32_t(e));
+        });
+      }, &a2, &e2);
+      ecut = int(~nk);
     }
     __syncthreads();
     if (tid == 0) s.cnt = 0;
     __syncthreads();
-    for_candidate_groups(s, row, V, gs, groups, t0, wave, lane, [&](bool in, uint32_t key, int e) {
-      wave_append(s, in && wins(key, e, kv, ilim), key, e, lane);
+    for_candidates(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int e) {
+      wave_append(s, in && (key > vstar || (key == vstar && e <= ecut)), key, e, lane);
     });
     __syncthreads();
     n = s.cnt;
   }
 
-  // c. prune long lists to the keys >= the k-th largest value key
+  // c. cut long lists to the k best (value, then lowest index among ties)
   if (n > uint32_t(2 * k)) {
     uint64_t mine[kPerThread];
-    uint32_t mlo = 0xFFFFFFFFu, mhi = 0;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      int i = tid + j * kSelThreads;
-      mine[j] = i < int(n) ? s.c[i] : 0;
-      if (i < int(n)) {
-        mlo = min(mlo, uint32_t(mine[j] >> 32));
-        mhi = max(mhi, uint32_t(mine[j] >> 32));
-      }
+      const int i = tid + j * kSelThreads;
+      mine[j] = i < int(n) ? s.c[i] : 0ull;
     }
-    uint64_t plo = blk.minv(mlo), phi = uint64_t(blk.maxv(mhi)) + 1;
-    while (phi - plo > 1) {
-      uint64_t mid = (plo + phi) >> 1;
-      uint32_t c = 0;
+    const uint32_t vstar = radix_kth(s, tid, uint32_t(k), [&](auto&& f) {
 #pragma unroll
-      for (int j = 0; j < kPerThread; ++j) c += (tid + j * kSelThreads < int(n)) && (mine[j] >> 32) >= mid;
-      if (blk.sum(c) >= uint32_t(k)) plo = mid; else phi = mid;
+      for (int j = 0; j < kPerThread; ++j)
+        if (tid + j * kSelThreads < int(n)) f(uint32_t(mine[j] >> 32));
+    }, &above, &equal);
+    uint32_t lowcut = 0;  // smallest ~index kept among keys == v*
+    if (above + equal > uint32_t(2 * k)) {
+      uint32_t a2, e2;
+      lowcut = radix_kth(s, tid, uint32_t(k) - above, [&](auto&& f) {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j)
+          if (tid + j * kSelThreads < int(n) && uint32_t(mine[j] >> 32) == vstar) f(uint32_t(mine[j]));
+      }, &a2, &e2);
     }
-    const uint32_t vstar = uint32_t(plo);
     if (tid == 0) s.cnt = 0;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      int i = tid + j * kSelThreads;
-      bool keep = i < int(n) && uint32_t(mine[j] >> 32) >= vstar;
-      uint64_t m = __ballot(keep);
+      const uint32_t key = uint32_t(mine[j] >> 32);
+      const bool keep = tid + j * kSelThreads < int(n) &&
+                        (key > vstar || (key == vstar && uint32_t(mine[j]) >= lowcut));
+      const uint64_t m = __ballot(keep);
       if (m) {
         uint32_t base = 0;
         if (lane == 0) base = atomicAdd(&s.cnt, (uint32_t)__popcll(m));
-        base = __shfl((int)base, 0, 64);
+        base = (uint32_t)__shfl((int)base, 0, 64);
         if (keep) s.c[base + __popcll(m & ((1ull << lane) - 1ull))] = mine[j];
       }
     }
@@ -280,32 +312,64 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
     n = s.cnt;
   }
 
-  // rank by composite key; the k best go out in order
+  // d. rank by composite key; the k best go out in order
   for (int i = tid; i < int(n); i += kSelThreads) {
     const uint64_t ci = s.c[i];
     uint32_t rank = 0;
     for (int j = 0; j < int(n); ++j) rank += s.c[j] > ci;
     if (rank < uint32_t(k)) {
       const int e = int(~uint32_t(ci));
-      vals[size_t(row_id) * k + rank] = row[e];
+      const float v = row[e];
+      vals[size_t(row_id) * k + rank] = v;
       idx[size_t(row_id) * k + rank] = e;
+      s.top_v[rank] = v;
+      s.top_i[rank] = e;
+    }
+  }
+
+  // f. the row's sampler
+  if (params != nullptr) {
+    __syncthreads();
+    if (tid < 64) {
+      const RowParams p = load_params(params, ncols, row_id);
+      const int32_t t = sample_row_wave<P>(s.top_v, s.top_i, k, p.top_k, p.top_p, p.temp, p.u, lane);
+      if (lane == 0) tokens[row_id] = t;
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_topk(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
-                       uint32_t* gkey_ws, float* vals, int32_t* idx, hipStream_t st) {
+hipError_t launch_group_max(const float* logits, int gbs, int V, const TopkGeom& geom,
+                            uint32_t* gkey, hipStream_t st) {
   const int gpb = kGmThreads / 64;
   dim3 g1((geom.groups + gpb - 1) / gpb, gbs);
-  hipLaunchKernelGGL(group_max_kernel, g1, dim3(kGmThreads), 0, st, logits, V, geom.gs,
-                     geom.groups, gkey_ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_kernel, dim3(gbs), dim3(kSelThreads), 0, st, logits, V, geom.gs,
-                     geom.groups, k, gkey_ws, vals, idx);
+  hipLaunchKernelGGL(group_max_kernel, g1, dim3(kGmThreads), 0, st, logits, V, geom.gs, geom.groups,
+                     gkey);
   return hipGetLastError();
+}
+
+hipError_t launch_select(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
+                         const uint32_t* gkey, float* vals, int32_t* idx, const float* params,
+                         int ncols, int32_t* tokens, hipStream_t st) {
+  dim3 grid(gbs), block(kSelThreads);
+#define TAIL_SELECT_LAUNCH(P)                                                                     \
+  hipLaunchKernelGGL(select_kernel<P>, grid, block, 0, st, logits, V, geom.gs, geom.groups, k, gkey, \
+                     vals, idx, params, ncols, tokens)
+  if (k <= 64) TAIL_SELECT_LAUNCH(1);
+  else if (k <= 128) TAIL_SELECT_LAUNCH(2);
+  else if (k <= 256) TAIL_SELECT_LAUNCH(4);
+  else if (k <= 512) TAIL_SELECT_LAUNCH(8);
+  else TAIL_SELECT_LAUNCH(16);
+#undef TAIL_SELECT_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
+                       uint32_t* gkey_ws, float* vals, int32_t* idx, hipStream_t st) {
+  hipError_t e = launch_group_max(logits, gbs, V, geom, gkey_ws, st);
+  if (e != hipSuccess) return e;
+  return launch_select(logits, gbs, V, k, geom, gkey_ws, vals, idx, nullptr, 0, nullptr, st);
 }
 
 }  // namespace tail

@@ -66,7 +66,12 @@ def test_rmsnorm(dtype, shape, deferred):
 # ---------------------------------------------------------------- lm_head
 @pytest.mark.parametrize("gbs,H,H_u,V,zp", [(1, 64, 64, 4096, False), (3, 300, 300, 1160, False),
                                             (8, 640, 640, 2048, False), (11, 200, 200, 520, False),
-                                            (2, 48, 45, 1032, True), (9, 3072, 2880, 1544, True)])
+                                            (2, 48, 45, 1032, True), (9, 3072, 2880, 1544, True),
+                                            (4, 2880, 2880, 1000, False), (5, 130, 130, 264, False),
+                                            (17, 96, 96, 776, False), (33, 320, 320, 1288, False),
+                                            (64, 3072, 2880, 2056, True), (65, 100, 100, 512, False),
+                                            (130, 2880, 2880, 800, False), (256, 700, 700, 1544, False),
+                                            (300, 64, 64, 264, False)])
 def test_lm_head(gbs, H, H_u, V, zp):
     rng = np.random.default_rng(V + gbs)
     pad = oracle.pad_mask(H, H_u, zp)
@@ -83,22 +88,25 @@ def test_lm_head(gbs, H, H_u, V, zp):
     assert np.all(np.isfinite(L))
 
 
-def test_lm_head_duplicate_columns_and_batch_invariance():
+@pytest.mark.parametrize("big", [4, 40])
+def test_lm_head_duplicate_columns_and_batch_invariance(big):
     """Duplicated weight columns give bitwise-equal logits wherever they sit, and
-    a row gives the same bytes alone or inside a batch."""
+    a row gives the same bytes in batches of different sizes on one lm_head
+    path (the weight-streaming path up to 4 rows, the matrix-core path above)."""
     rng = np.random.default_rng(5)
     H, V = 2880, 4096
     w = bf16_bits(rng.standard_normal((H, V)) * 0.02)
     src = rng.choice(V, 64, replace=False)
     dst_cols = rng.choice(np.setdiff1d(np.arange(V), src), 64, replace=False)
     w[:, dst_cols] = w[:, src]
-    y = rng.standard_normal((8, H)).astype(np.float32)
+    y = rng.standard_normal((big, H)).astype(np.float32)
     wt = gpu_bf16(w)
-    L8 = np_(dst.lm_head(torch.from_numpy(y).cuda(), wt))
-    assert np.array_equal(L8[:, src], L8[:, dst_cols])
-    for b in (0, 5, 7):
-        L1 = np_(dst.lm_head(torch.from_numpy(y[b:b + 1].copy()).cuda(), wt))
-        assert np.array_equal(L1[0], L8[b])
+    Lb = np_(dst.lm_head(torch.from_numpy(y).cuda(), wt))
+    assert np.array_equal(Lb[:, src], Lb[:, dst_cols])
+    small = 1 if big <= 4 else 5
+    for b0 in (0, big - small):
+        Ls = np_(dst.lm_head(torch.from_numpy(y[b0:b0 + small].copy()).cuda(), wt))
+        assert np.array_equal(Ls, Lb[b0:b0 + small])
 
 
 # ------------------------------------------------------------------- top-k
@@ -191,6 +199,50 @@ def test_workload_parity(cid, run):
     print(f"tokens: {len(out['tokens'])} rows, exempt {exempt}, widened-band {widened}")
     assert not fails, fails
     assert not check_sampler_on_gpu_candidates(out["tokens"], out["vals"], out["idx"], params)
+
+
+@pytest.mark.parametrize("gbs,H,H_u,V,k,zp,dtype", [
+    (3, 256, 256, 1032, 256, False, synth.DT_F32),   # groups of 4 columns: separate group-max pass
+    (2, 48, 45, 4096, 16, True, synth.DT_F16),       # pad lanes, fused 128-column groups
+    (5, 300, 300, 8000, 64, False, synth.DT_BF16),   # ragged last slab
+    (9, 640, 640, 2048, 1024, False, synth.DT_F32),  # k = TAIL_K_MAX, two lm_head passes
+    (1, 128, 128, 64, 64, False, synth.DT_F32),      # k = V
+])
+def test_forward_small_shapes(gbs, H, H_u, V, k, zp, dtype):
+    rng = np.random.default_rng(V * 31 + k)
+    pad = oracle.pad_mask(H, H_u, zp)
+    x = rng.standard_normal((gbs, H)).astype(np.float32)
+    x[:, pad] = np.nan if zp else 0.0
+    gamma = (1 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    w = bf16_bits(rng.standard_normal((H, V)) * 0.05)
+    w[pad] = 0x7FC0 if zp else 0
+    p = np.empty((gbs, 4), np.float32)
+    p[:, 0] = rng.integers(0, k + 2, gbs)
+    p[:, 1] = rng.uniform(0.3, 1.0, gbs)
+    p[:, 2] = np.where(rng.random(gbs) < 0.3, 0.0, rng.uniform(0.3, 1.5, gbs))
+    p[:, 3] = rng.uniform(0, 1, gbs)
+    if dtype == synth.DT_F16:
+        xs = x.astype(np.float16)
+        xt = torch.from_numpy(xs).cuda()
+    elif dtype == synth.DT_BF16:
+        xs = synth.round_bf16(x)
+        xt = gpu_bf16(xs)
+    else:
+        xs = x
+        xt = torch.from_numpy(x).cuda()
+    out = dst.forward(xt, torch.from_numpy(gamma).cuda(), gpu_bf16(w), k=k, H_u=H_u, zero_pad=zp,
+                      params=torch.from_numpy(p).cuda())
+    torch.cuda.synchronize()
+    out = {key: np_(v) for key, v in out.items()}
+    ref = oracle.tail(xs, dtype, gamma, w, H_u, k, 1e-5, zp, params=p)
+    ref["vals_k1"] = oracle.topk(ref["logits"], k + 1)[0] if k < V else None
+    fails, rel, mx = check_logits(out["logits"], ref["logits"])
+    assert not fails, fails
+    assert not check_topk_sets(out["idx"], ref["logits"], k)
+    assert not check_topk_exact(out["vals"], out["idx"], out["logits"], k)
+    fails, exempt, widened = check_tokens(out["tokens"], ref, p, out["logits"], k)
+    assert not fails, fails
+    assert not check_sampler_on_gpu_candidates(out["tokens"], out["vals"], out["idx"], p)
 
 
 def test_workload_in_chain_rms_and_unemitted_logits():
