@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "tail tokens/s at gbs 1/8/64/256, V=201088; lm_head HBM GB/s & MFMA % of peak"
 HBM_PEAK = 8000.0  # GB/s, MI355X HBM3E
-COUNTERS = os.path.join(ROOT, "profiles", "lm_head_gemv_gbs1_counters.md")
+COUNTERS = os.path.join(ROOT, "profiles", "rmsnorm_lm_head_gbs1_counters.md")
 
 
 def log(msg):
@@ -43,7 +43,23 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of exactly 1 GiB, three times: the HBM
+    byte counters of this known-size copy scale the lm_head's counter reads."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(copy_calibration_bytes=n, copies=3)), flush=True)
 
 
 def kernel_source_hash():
@@ -55,8 +71,9 @@ def kernel_source_hash():
 
 
 def counter_traffic():
-    """Per-launch HBM bytes of the gbs-1 lm_head kernel from the committed
-    rocprofv3 counter summary, or None if absent or taken on other sources."""
+    """Per-launch HBM bytes (fetch + write, each scaled by the copy
+    calibration) of the gbs-1 RMSNorm+lm_head kernel, from the committed
+    rocprofv3 counter summary; None if absent or taken on other sources."""
     if not os.path.exists(COUNTERS):
         return None
     text = open(COUNTERS).read()
@@ -109,30 +126,35 @@ def bench_workload(cid, args, torch, np):
                     emit_logits=False)
     t_step = time_loop(torch, lambda: f(g["hidden"], g["gamma"], g["w_t"], g["params"]),
                        args.steps, args.warmup)
-    # stage by stage, same kernels and launch shapes as inside tail_forward
-    y, r = dst.rmsnorm(g["hidden"], g["gamma"], inp.H_u, inp.eps, inp.zero_pad, deferred=True)
+    # stage by stage.  rmsnorm_lm_head runs the same kernels and launch shapes
+    # as tail_forward's first stage (there they also emit the group maxima);
+    # topk and sample are the standalone calls (inside tail_forward the group
+    # maxima come from the lm_head epilogue and the sampler is fused into the
+    # top-k kernel).
     logits = torch.empty((inp.gbs, inp.V), dtype=torch.float32, device="cuda")
-    vals, idx = dst.topk(dst.lm_head(y, g["w_t"], inp.H_u, inp.zero_pad, row_scale=r, out=logits), inp.k)
-    t_norm = time_loop(torch, lambda: dst.rmsnorm(g["hidden"], g["gamma"], inp.H_u, inp.eps,
-                                                  inp.zero_pad, deferred=True, out_y=y, out_r=r),
-                       args.steps, args.warmup)
-    t_lm = time_loop(torch, lambda: dst.lm_head(y, g["w_t"], inp.H_u, inp.zero_pad, row_scale=r,
-                                                out=logits), args.steps, args.warmup)
-    ws = torch.empty(dst.workspace_size(inp.gbs, 1, 1, inp.V, inp.k, dst.EMIT_LOGITS),
+    r = torch.empty((inp.gbs,), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dst.workspace_size(inp.gbs, inp.H, inp.H_u, inp.V, inp.k, dst.EMIT_LOGITS),
                      dtype=torch.uint8, device="cuda")
+    norm_lm = lambda: dst.rmsnorm_lm_head(g["hidden"], g["gamma"], g["w_t"], inp.H_u, inp.eps,
+                                          inp.zero_pad, True, out=logits, out_r=r, ws=ws)
+    norm_lm()
+    vals, idx = dst.topk(logits, inp.k, ws=ws)
+    t_lm = time_loop(torch, norm_lm, args.steps, args.warmup)
     t_topk = time_loop(torch, lambda: dst.topk(logits, inp.k, vals, idx, ws), args.steps, args.warmup)
     tok = torch.empty((inp.gbs,), dtype=torch.int32, device="cuda")
     t_samp = time_loop(torch, lambda: dst.sample(vals, idx, g["params"], tok), args.steps, args.warmup)
-    w_bytes = inp.H_u * inp.V * 2
-    lm_bytes = w_bytes + inp.gbs * inp.H * 4 + inp.gbs * 4 + inp.gbs * inp.V * 4
+    hid_bytes = inp.hidden.dtype.itemsize
+    # algorithmic bytes: the real lanes of weight, hidden and gamma once, the
+    # logits and the row scale written once
+    lm_bytes = (inp.H_u * inp.V * 2 + inp.gbs * inp.H_u * hid_bytes + inp.H_u * 4 +
+                inp.gbs * inp.V * 4 + inp.gbs * 4)
     flops = 2.0 * inp.gbs * inp.H_u * inp.V
     res = dict(gbs=inp.gbs, tokens_per_s=inp.gbs / t_step, steps_per_s=1.0 / t_step,
                ms_per_step=t_step * 1e3,
-               stage_us=dict(rmsnorm=t_norm * 1e6, lm_head=t_lm * 1e6, topk=t_topk * 1e6,
-                             sample=t_samp * 1e6),
+               stage_us=dict(rmsnorm_lm_head=t_lm * 1e6, topk=t_topk * 1e6, sample=t_samp * 1e6),
                lm_head_gbs=lm_bytes / t_lm / 1e9, lm_head_tflops=flops / t_lm / 1e12,
                lm_head_bytes=lm_bytes)
-    del g, f, logits, ws
+    del g, f, logits, ws, r
     torch.cuda.empty_cache()
     return inp, run, res
 
@@ -160,6 +182,9 @@ def cpu_baseline(inp, run, budget_s=12.0):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -187,8 +212,9 @@ def main():
     traffic = counter_traffic()
     roof = dict(bound="hbm", achieved=head["lm_head_gbs"], peak=HBM_PEAK, unit="GB/s",
                 frac=head["lm_head_gbs"] / HBM_PEAK, traffic=traffic,
-                kernel="lm_head gemv (gbs 1)", bytes_per_launch=head["lm_head_bytes"],
-                launch_us=head["stage_us"]["lm_head"])
+                kernel="gemv_kernel<1,2,4,6>: RMSNorm-fused weight-streaming lm_head, gbs 1",
+                bytes_per_launch=head["lm_head_bytes"],
+                launch_us=head["stage_us"]["rmsnorm_lm_head"])
     out = dict(metric=METRIC, value=head["tokens_per_s"], unit="tokens/s", n_gpus=1,
                steps=args.steps, warmup=args.warmup, ms_per_step=head["ms_per_step"],
                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="fp32",

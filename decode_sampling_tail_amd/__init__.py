@@ -7,7 +7,8 @@ synchronize.  There is no CPU fallback: if the library is not built, loading
 it raises.
 
 The names mirror the C entry points in include/tail.h:
-rmsnorm, lm_head, topk, sample, forward, workspace_size, status_string.
+rmsnorm, lm_head, rmsnorm_lm_head, topk, sample, forward, workspace_size,
+status_string.
 """
 from __future__ import annotations
 
@@ -22,8 +23,8 @@ F32, F16, BF16 = 0, 1, 2
 EMIT_LOGITS, ZERO_PAD, DEFERRED_RMS = 1, 2, 4
 K_MAX, GBS_MAX, H_MAX = 1024, 4096, 65536
 
-EXPORTS = ("tail_rmsnorm", "tail_lm_head", "tail_topk", "tail_sample", "tail_forward",
-           "tail_workspace_size", "tail_status_string")
+EXPORTS = ("tail_rmsnorm", "tail_lm_head", "tail_rmsnorm_lm_head", "tail_topk", "tail_sample",
+           "tail_forward", "tail_workspace_size", "tail_status_string")
 
 _lib = None
 
@@ -44,6 +45,7 @@ def lib() -> ctypes.CDLL:
         vp, i, u, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_float, ctypes.c_size_t
         L.tail_rmsnorm.argtypes = [vp, i, vp, i, i, i, f, u, vp, vp, vp]
         L.tail_lm_head.argtypes = [vp, vp, vp, i, i, i, i, u, vp, vp, sz, vp]
+        L.tail_rmsnorm_lm_head.argtypes = [vp, i, vp, vp, i, i, i, i, f, u, vp, vp, vp, sz, vp]
         L.tail_topk.argtypes = [vp, i, i, i, vp, vp, vp, sz, vp]
         L.tail_sample.argtypes = [vp, vp, i, i, vp, i, vp, vp]
         L.tail_forward.argtypes = [vp, i, vp, vp, i, i, i, i, i, f, u, vp, i, vp, vp, vp, vp, vp, sz, vp]
@@ -51,7 +53,8 @@ def lib() -> ctypes.CDLL:
         L.tail_workspace_size.restype = sz
         L.tail_status_string.argtypes = [i]
         L.tail_status_string.restype = ctypes.c_char_p
-        for name in ("tail_rmsnorm", "tail_lm_head", "tail_topk", "tail_sample", "tail_forward"):
+        for name in ("tail_rmsnorm", "tail_lm_head", "tail_rmsnorm_lm_head", "tail_topk",
+                     "tail_sample", "tail_forward"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -142,6 +145,25 @@ def lm_head(y, w_t, H_u=None, zero_pad=False, row_scale=None, out=None, ws=None)
     _call("tail_lm_head", _ptr(y), _ptr(_weight(w_t)), _ptr(row_scale), gbs, H, H_u, V,
           _flags(zero_pad), _ptr(logits), _ptr(ws), ws.numel(), _stream(dev))
     return logits
+
+
+def rmsnorm_lm_head(hidden, gamma, w_t, H_u=None, eps=1e-5, zero_pad=False, deferred=True, out=None,
+                    out_r=None, ws=None):
+    """tail_rmsnorm_lm_head: (logits [gbs,V] fp32, r [gbs] fp32)."""
+    torch = _torch()
+    dev = _dev(hidden)
+    gbs, H = hidden.shape
+    V = w_t.shape[1]
+    H_u = H if H_u is None else H_u
+    flags = _flags(zero_pad, deferred)
+    logits = out if out is not None else torch.empty((gbs, V), dtype=torch.float32, device=dev)
+    r = out_r if out_r is not None else torch.empty((gbs,), dtype=torch.float32, device=dev)
+    if ws is None:
+        n = workspace_size(gbs, H, H_u, V, 1, flags | EMIT_LOGITS)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    _call("tail_rmsnorm_lm_head", _ptr(hidden), _hidden_dtype(hidden), _ptr(gamma), _ptr(_weight(w_t)),
+          gbs, H, H_u, V, eps, flags, _ptr(logits), _ptr(r), _ptr(ws), ws.numel(), _stream(dev))
+    return logits, r
 
 
 def topk(logits, k, out_vals=None, out_idx=None, ws=None):

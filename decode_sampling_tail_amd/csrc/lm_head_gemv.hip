@@ -1,31 +1,45 @@
 // lm_head contraction, weight-streaming form for small batches (GPT-OSS tail
 // API page, parameter "lm_head_weight_t": [H, V] bf16, already transposed and
-// C-contiguous).
+// C-contiguous), optionally with the final RMSNorm fused into its prologue
+// (parameters "gamma", "eps", "hidden_actual", "deferred_rms").
 //
-// logits[b, v] = row_scale[b] * sum_h y[b, h] * W[h, v]
+// logits[b, v] = scale[b] * sum_u y[b, u] * W[h(u), v]
 //
-// The weight (H_u * V * 2 bytes, 1.16 GB for GPT-OSS) is read exactly once;
+// The weight (K * V * 2 bytes, 1.16 GB for GPT-OSS) is read exactly once;
 // that read is the roofline of the whole tail at small batch.
 //
-// Mapping: a 512-thread workgroup (8 waves) owns a slab of 512 consecutive
+// Mapping: a workgroup of W waves (8 by default) owns a slab of 512 consecutive
 // vocabulary columns; lane l of every wave owns columns 8l..8l+7 of the slab,
-// which it reads as one 16-byte load per weight row, so each wave reads a
-// contiguous 1 KB of a row per load.  The 8 waves split the (unpadded) hidden
-// lanes into 8 contiguous ranges; each keeps NB x 8 fp32 partial sums for the
-// NB batch rows of this pass, reading y[b, h] through the scalar cache (the
-// row index is wave-uniform).  Partials are combined through LDS in a fixed
-// tree, ((p0+p4)+(p2+p6)) + ((p1+p5)+(p3+p7)), so a column's sum depends only
-// on H_u and never on the column's position or on the other batch rows.
+// read as one non-temporal 16-byte load per weight row (a wave reads 1 KB
+// of a row per load).  The W waves split the K contraction lanes into W
+// contiguous ranges and keep NB x 8 fp32 partial sums each; loads run one
+// batch of U rows ahead of the FMAs.  Partials are combined through LDS in a
+// fixed tree (step d adds wave w + d into wave w, d = W/2 .. 1; for W = 8:
+// ((p0+p4)+(p2+p6)) + ((p1+p5)+(p3+p7))), so a column's sum depends only on
+// K and the shape, never on the column's position or on the other rows.
+//
+// Activations: SRC < 0 reads a given fp32 y [gbs, H] through the scalar
+// cache (row index wave-uniform), scale = row_scale (or 1).  SRC = hidden
+// dtype (0 fp32, 1 fp16, 2 bf16) fuses the RMSNorm: the prologue widens the
+// NB hidden rows exactly, accumulates each row's sum of squares in fp64 in a
+// fixed order (per wave over its lanes, then the W wave partials in order),
+// and stores y compacted over the K lanes in LDS, with
+// r = fp32(1 / sqrt(sum / H_u + eps)).  Deferred: each wave fills only its
+// own K range with y = x * gamma, so no barrier delays the weight stream, and
+// r (scale) is finished in the epilogue.  In-chain: the whole row's r comes
+// first and y = (x * r) * gamma (scale = 1).
 #include "tail_internal.h"
+
+#include <hip/hip_fp16.h>
 
 namespace tail {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
 constexpr int kSlab = 512;  // columns per workgroup
-constexpr int kUnroll = 8;  // weight rows in flight per lane
 constexpr int kMaxNB = 8;   // batch rows per pass
+// default shape: waves per workgroup and weight rows per load batch
+constexpr int kWaves = 4;
+constexpr int kUnroll = 6;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -39,24 +53,152 @@ __device__ inline uint4 load_stream(const uint16_t* p) {
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-template <int NB>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const float* __restrict__ y, int ldy,
-                                                        const uint16_t* __restrict__ w,
-                                                        const float* __restrict__ row_scale,
-                                                        int H_u, int pad_s, int V,
-                                                        float* __restrict__ logits,
-                                                        uint32_t* __restrict__ gkey, int groups,
-                                                        int b0) {
-  __shared__ float4 s_red[4][NB][kSlab / 4];
+template <int DT>
+__device__ inline float load_hidden(const void* p, size_t i) {
+  if constexpr (DT == 0) {
+    return static_cast<const float*>(p)[i];
+  } else if constexpr (DT == 1) {
+    return __half2float(static_cast<const __half*>(p)[i]);
+  } else {
+    const uint32_t b = static_cast<const uint16_t*>(p)[i];
+    return __uint_as_float(b << 16);
+  }
+}
+
+__device__ inline double wave_sum(double v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+struct GemvArgs {
+  const void* src;         // y fp32 [gbs, ldsrc] (SRC < 0) or hidden [gbs, ldsrc] (fused)
+  int ldsrc;               // row stride of src (H)
+  const float* gamma;      // fused only
+  float eps;               // fused only
+  int H_u;                 // fused only: mean-square divisor
+  int deferred;            // fused only
+  const uint16_t* w;
+  const float* row_scale;  // SRC < 0 only (may be NULL)
+  int K, pad_s, V;
+  FastDiv pdiv;
+  float* logits;
+  float* r_out;            // fused only (may be NULL): per-row r
+  uint32_t* gkey;
+  int groups, b0;
+};
+
+template <int NB, int SRC, int W = kWaves, int U = kUnroll>
+__global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
+  constexpr int kThreads = W * 64;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float4* s_red = reinterpret_cast<float4*>(smem);                         // [W/2][NB][kSlab/4]
+  float* s_y = reinterpret_cast<float*>(smem + (W / 2) * NB * kSlab * 4);  // [NB][K] (fused)
+  __shared__ double s_part[NB][W];
+
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
   const int col = blockIdx.x * kSlab + lane * 8;
-  const bool act = col < V;
+  const bool act = col < a.V;
+  const int K = a.K, V = a.V, pad_s = a.pad_s;
 
-  const int u0 = (wave * H_u) / kWaves;
-  const int u1 = ((wave + 1) * H_u) / kWaves;
-  int h = phys_lane(u0, pad_s);
+  const int u0 = (wave * K) / W;
+  const int u1 = ((wave + 1) * K) / W;
+  int h = pad_s ? u0 + int(fastdiv(uint32_t(u0), a.pdiv)) : u0;
   int gpos = pad_s ? h % pad_s : 0;
+  const uint16_t* wcol = a.w + col;
+
+  uint4 wv[U];
+  int hh[U];
+  auto load_batch = [&](int u, uint4 (&dst)[U], int (&hd)[U]) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      hd[j] = h;
+      dst[j] = make_uint4(0, 0, 0, 0);
+      if (u + j < u1 && act) dst[j] = load_stream(wcol + size_t(h) * V);
+      ++h;
+      if (pad_s && ++gpos == pad_s - 1) {
+        ++h;
+        gpos = 0;
+      }
+    }
+  };
+  load_batch(u0, wv, hh);  // in flight while the prologue runs
+
+  float scale[NB];
+  bool scale_at_end = false;  // deferred fused RMSNorm: r is finished in the epilogue
+  if constexpr (SRC >= 0) {
+    const size_t rowbase = size_t(a.b0) * a.ldsrc;
+    if (a.deferred) {
+      // each wave builds only its own slice [u0, u1) of the y table and its
+      // partial sum of squares: no workgroup barrier before the main loop
+      // loads go out in bursts of kBurst lanes per thread (one memory
+      // latency per burst rather than one per element)
+      constexpr int kBurst = 16;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        double ss = 0.0;
+        for (int c0 = u0; c0 < u1; c0 += 64 * kBurst) {
+          float x[kBurst], g[kBurst];
+#pragma unroll
+          for (int i = 0; i < kBurst; ++i) {
+            const int u = c0 + lane + 64 * i;
+            x[i] = 0.0f;
+            g[i] = 0.0f;
+            if (u < u1) {
+              const int hp = pad_s ? u + int(fastdiv(uint32_t(u), a.pdiv)) : u;
+              x[i] = load_hidden<SRC>(a.src, rowbase + size_t(b) * a.ldsrc + hp);
+              g[i] = a.gamma[hp];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < kBurst; ++i) {
+            const int u = c0 + lane + 64 * i;
+            ss = fma(double(x[i]), double(x[i]), ss);
+            if (u < u1) s_y[b * K + u] = x[i] * g[i];
+          }
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) s_part[b][wave] = ss;
+        scale[b] = 1.0f;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      scale_at_end = true;
+    } else {
+      // in-chain: r is needed before the contraction, so the whole row first
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        double ss = 0.0;
+        for (int u = tid; u < K; u += kThreads) {
+          const int hp = pad_s ? u + int(fastdiv(uint32_t(u), a.pdiv)) : u;
+          const float x = load_hidden<SRC>(a.src, rowbase + size_t(b) * a.ldsrc + hp);
+          ss = fma(double(x), double(x), ss);
+          s_y[b * K + u] = x;
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) s_part[b][wave] = ss;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        double tot = 0.0;  // the wave partials in wave order
+#pragma unroll
+        for (int w = 0; w < W; ++w) tot += s_part[b][w];
+        const float r = float(1.0 / sqrt(tot / double(a.H_u) + double(a.eps)));
+        scale[b] = 1.0f;
+        for (int u = tid; u < K; u += kThreads) {
+          const int hp = pad_s ? u + int(fastdiv(uint32_t(u), a.pdiv)) : u;
+          s_y[b * K + u] = (s_y[b * K + u] * r) * a.gamma[hp];
+        }
+        if (tid == 0 && a.r_out) a.r_out[a.b0 + b] = r;
+      }
+      __syncthreads();
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) scale[b] = a.row_scale ? a.row_scale[a.b0 + b] : 1.0f;
+  }
 
   float acc[NB][8];
 #pragma unroll
@@ -64,53 +206,58 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const float* __restrict_
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[b][c] = 0.0f;
 
-  const uint16_t* wcol = w + col;
-  const float* yb = y + size_t(b0) * ldy;
-
-  for (int u = u0; u < u1; u += kUnroll) {
-    uint4 wv[kUnroll];
-    int hh[kUnroll];
+  const float* yg = static_cast<const float*>(a.src) + size_t(a.b0) * a.ldsrc;
+  for (int u = u0; u < u1; u += U) {
+    uint4 nx[U];
+    int nh[U];
+    if (u + U < u1) load_batch(u + U, nx, nh);
+    // the batch's activations first (rows past the range read as 0 and their
+    // weights were not loaded, so they add exact zeros), then the FMAs
+    float yv[NB][U];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      hh[j] = h;
-      wv[j] = make_uint4(0, 0, 0, 0);
-      if (u + j < u1 && act) wv[j] = load_stream(wcol + size_t(h) * V);
-      ++h;
-      if (pad_s && ++gpos == pad_s - 1) {
-        ++h;
-        gpos = 0;
-      }
-    }
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      if (u + j < u1) {
-        float wf[8] = {bf_lo(wv[j].x), bf_hi(wv[j].x), bf_lo(wv[j].y), bf_hi(wv[j].y),
-                       bf_lo(wv[j].z), bf_hi(wv[j].z), bf_lo(wv[j].w), bf_hi(wv[j].w)};
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float yv = yb[size_t(b) * ldy + hh[j]];
-#pragma unroll
-          for (int c = 0; c < 8; ++c) acc[b][c] = fmaf(yv, wf[c], acc[b][c]);
+      for (int j = 0; j < U; ++j) {
+        yv[b][j] = 0.0f;
+        if (u + j < u1) {
+          if constexpr (SRC >= 0) yv[b][j] = s_y[b * K + u + j];
+          else yv[b][j] = yg[size_t(b) * a.ldsrc + hh[j]];
         }
       }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const float wf[8] = {bf_lo(wv[j].x), bf_hi(wv[j].x), bf_lo(wv[j].y), bf_hi(wv[j].y),
+                           bf_lo(wv[j].z), bf_hi(wv[j].z), bf_lo(wv[j].w), bf_hi(wv[j].w)};
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[b][c] = fmaf(yv[b][j], wf[c], acc[b][c]);
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      wv[j] = nx[j];
+      hh[j] = nh[j];
     }
   }
 
-  // fixed-order tree over the 8 waves: step d pairs wave w with w + d
+  // fixed-order tree over the waves: step d pairs wave w with w + d
 #pragma unroll
-  for (int d = 4; d >= 1; d >>= 1) {
+  for (int d = W / 2; d >= 1; d >>= 1) {
     if (wave >= d && wave < 2 * d) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        s_red[wave - d][b][lane * 2] = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
-        s_red[wave - d][b][lane * 2 + 1] = make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
+        s_red[((wave - d) * NB + b) * (kSlab / 4) + lane * 2] =
+            make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+        s_red[((wave - d) * NB + b) * (kSlab / 4) + lane * 2 + 1] =
+            make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
       }
     }
     __syncthreads();
     if (wave < d) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        float4 p = s_red[wave][b][lane * 2], q = s_red[wave][b][lane * 2 + 1];
+        const float4 p = s_red[(wave * NB + b) * (kSlab / 4) + lane * 2];
+        const float4 q = s_red[(wave * NB + b) * (kSlab / 4) + lane * 2 + 1];
         acc[b][0] += p.x; acc[b][1] += p.y; acc[b][2] += p.z; acc[b][3] += p.w;
         acc[b][4] += q.x; acc[b][5] += q.y; acc[b][6] += q.z; acc[b][7] += q.w;
       }
@@ -119,18 +266,29 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const float* __restrict_
   }
 
   if (wave == 0) {
+    if (scale_at_end) {  // every wave's partial sum of squares is visible after the tree
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        double tot = 0.0;  // the wave partials in wave order
+#pragma unroll
+        for (int w = 0; w < W; ++w) tot += s_part[b][w];
+        const float r = float(1.0 / sqrt(tot / double(a.H_u) + double(a.eps)));
+        scale[b] = r;
+        if (lane == 0 && blockIdx.x == 0 && a.r_out) a.r_out[a.b0 + b] = r;
+      }
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const float s = row_scale ? row_scale[b0 + b] : 1.0f;
+      const float s = scale[b];
       float o[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) o[c] = acc[b][c] * s;
       if (act) {
-        float4* out = reinterpret_cast<float4*>(logits + size_t(b0 + b) * V + col);
+        float4* out = reinterpret_cast<float4*>(a.logits + size_t(a.b0 + b) * V + col);
         out[0] = make_float4(o[0], o[1], o[2], o[3]);
         out[1] = make_float4(o[4], o[5], o[6], o[7]);
       }
-      if (gkey) {  // maxima of the 64-column groups: 8 lanes each
+      if (a.gkey) {  // maxima of the 64-column groups: 8 lanes each
         uint32_t m = 0;
         if (act) {
 #pragma unroll
@@ -139,43 +297,104 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const float* __restrict_
 #pragma unroll
         for (int off = 1; off < 8; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
         const int g = blockIdx.x * (kSlab / kFusedGroup) + lane / 8;
-        if ((lane & 7) == 0 && g < groups) gkey[size_t(b0 + b) * groups + g] = m;
+        if ((lane & 7) == 0 && g < a.groups) a.gkey[size_t(a.b0 + b) * a.groups + g] = m;
       }
     }
   }
 }
 
-template <int NB>
-void launch_nb(dim3 grid, hipStream_t st, const float* y, int ldy, const uint16_t* w,
-               const float* rs, int H_u, int pad_s, int V, float* logits, uint32_t* gkey,
-               int groups, int b0) {
-  hipLaunchKernelGGL(gemv_kernel<NB>, grid, dim3(kThreads), 0, st, y, ldy, w, rs, H_u, pad_s, V,
-                     logits, gkey, groups, b0);
+// Dynamic LDS above 64 KB needs the kernel's limit raised once per process.
+template <int NB, int SRC>
+hipError_t raise_lds_limit() {
+  static const hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemv_kernel<NB, SRC>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+  return e;
+}
+
+template <int SRC>
+hipError_t launch_pass(int nb, dim3 grid, hipStream_t st, const GemvArgs& a) {
+  const size_t lds = size_t(kWaves / 2) * nb * kSlab * 4 + (SRC >= 0 ? size_t(nb) * a.K * 4 : 0);
+#define TAIL_GEMV(NB)                                                                   \
+  do {                                                                                  \
+    if (lds > 64 * 1024) {                                                              \
+      const hipError_t le = raise_lds_limit<NB, SRC>();                                 \
+      if (le != hipSuccess) return le;                                                  \
+    }                                                                                   \
+    hipLaunchKernelGGL((gemv_kernel<NB, SRC>), grid, dim3(kWaves * 64), lds, st, a);    \
+  } while (0)
+  switch (nb) {
+    case 1: TAIL_GEMV(1); break;
+    case 2: TAIL_GEMV(2); break;
+    case 3: TAIL_GEMV(3); break;
+    case 4: TAIL_GEMV(4); break;
+    case 5: TAIL_GEMV(5); break;
+    case 6: TAIL_GEMV(6); break;
+    case 7: TAIL_GEMV(7); break;
+    default: TAIL_GEMV(8); break;
+  }
+#undef TAIL_GEMV
+  return hipGetLastError();
 }
 
 }  // namespace
 
+bool gemv_fusable(int gbs, int K) {
+  return gbs <= kGemvMaxBatch &&
+         size_t(kWaves / 2) * gbs * kSlab * 4 + size_t(gbs) * K * 4 <= 96 * 1024;
+}
+
 hipError_t launch_lm_head_gemv(const float* y, int ldy, const uint16_t* w, const float* row_scale,
-                               int gbs, int H_u, int pad_s, int V, float* logits, uint32_t* gkey,
+                               int gbs, int K, int pad_s, int V, float* logits, uint32_t* gkey,
                                hipStream_t st) {
+  GemvArgs a{};
+  a.src = y;
+  a.ldsrc = ldy;
+  a.w = w;
+  a.row_scale = row_scale;
+  a.K = K;
+  a.pad_s = pad_s;
+  a.V = V;
+  a.pdiv = make_fastdiv(pad_s > 1 ? uint32_t(pad_s - 1) : 1u);
+  a.logits = logits;
+  a.gkey = gkey;
+  a.groups = (V + kFusedGroup - 1) / kFusedGroup;
   dim3 grid((V + kSlab - 1) / kSlab);
-  const int groups = (V + kFusedGroup - 1) / kFusedGroup;
   for (int b0 = 0; b0 < gbs; b0 += kMaxNB) {
-    int nb = gbs - b0 < kMaxNB ? gbs - b0 : kMaxNB;
-    switch (nb) {
-      case 1: launch_nb<1>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
-      case 2: launch_nb<2>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
-      case 3: launch_nb<3>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
-      case 4: launch_nb<4>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
-      case 5: launch_nb<5>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
-      case 6: launch_nb<6>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
-      case 7: launch_nb<7>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
-      default: launch_nb<8>(grid, st, y, ldy, w, row_scale, H_u, pad_s, V, logits, gkey, groups, b0); break;
-    }
-    hipError_t e = hipGetLastError();
+    a.b0 = b0;
+    const int nb = gbs - b0 < kMaxNB ? gbs - b0 : kMaxNB;
+    const hipError_t e = launch_pass<-1>(nb, grid, st, a);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_norm_gemv(const void* hidden, int dtype, const float* gamma, int gbs, int H,
+                            int H_u, int K, int pad_s, float eps, bool deferred, const uint16_t* w,
+                            int V, float* logits, float* r_out, uint32_t* gkey, hipStream_t st) {
+  GemvArgs a{};
+  a.src = hidden;
+  a.ldsrc = H;
+  a.gamma = gamma;
+  a.eps = eps;
+  a.H_u = H_u;
+  a.deferred = deferred ? 1 : 0;
+  a.w = w;
+  a.K = K;
+  a.pad_s = pad_s;
+  a.V = V;
+  a.pdiv = make_fastdiv(pad_s > 1 ? uint32_t(pad_s - 1) : 1u);
+  a.logits = logits;
+  a.r_out = r_out;
+  a.gkey = gkey;
+  a.groups = (V + kFusedGroup - 1) / kFusedGroup;
+  a.b0 = 0;
+  dim3 grid((V + kSlab - 1) / kSlab);
+  switch (dtype) {
+    case 0: return launch_pass<0>(gbs, grid, st, a);
+    case 1: return launch_pass<1>(gbs, grid, st, a);
+    default: return launch_pass<2>(gbs, grid, st, a);
+  }
 }
 
 }  // namespace tail

@@ -151,25 +151,36 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
     r = float(1.0 / sqrt(tot / double(H_u) + double(eps)));
     if (tid == 0 && r_out) r_out[row] = r;
   }
-  for (int u = tid; u < Kp; u += kThreads) {
-    float y = 0.0f;
-    if (u < K) {
-      const int h = pad_s ? u + int(fastdiv(uint32_t(u), pdiv)) : u;
-      const float x = load_hidden<DT>(src, base + h);
-      if constexpr (NORM) {
-        const float g = gamma[h];
-        y = deferred ? x * g : (x * r) * g;
-      } else {
-        y = x;
+  for (int u0 = 0; u0 < Kp; u0 += kBurst) {  // one memory latency per burst
+    float x[kPer], g[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = u0 + tid + i * kThreads;
+      x[i] = 0.0f;
+      g[i] = 1.0f;
+      if (u < K) {
+        const int h = pad_s ? u + int(fastdiv(uint32_t(u), pdiv)) : u;
+        x[i] = load_hidden<DT>(src, base + h);
+        if constexpr (NORM) g[i] = gamma[h];
       }
     }
-    const int slot = k_slot(u);
-    float rem = y;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint16_t b = bf16_rne(rem);
-      act[(size_t(t) * rows_pad + row) * Kp + slot] = b;
-      rem = rem - bf16_val(b);
+    for (int i = 0; i < kPer; ++i) {
+      const int u = u0 + tid + i * kThreads;
+      if (u >= Kp) continue;
+      float y = 0.0f;
+      if (u < K) {
+        if constexpr (NORM) y = deferred ? x[i] * g[i] : (x[i] * r) * g[i];
+        else y = x[i];
+      }
+      const int slot = k_slot(u);
+      float rem = y;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint16_t b = bf16_rne(rem);
+        act[(size_t(t) * rows_pad + row) * Kp + slot] = b;
+        rem = rem - bf16_val(b);
+      }
     }
   }
 }

@@ -22,11 +22,6 @@
 
 namespace tail {
 
-__device__ inline int wave_min_i32(int v) {
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
-  return v;
-}
-
 // vals / ix: the row's candidates in descending order (global or LDS memory).
 // Returns the token on every lane.
 template <int P, typename VP, typename IP>
@@ -62,24 +57,22 @@ __device__ inline int32_t sample_row_wave(VP vals, IP ix, int k, float top_k, fl
     return __shfl(mine, i / P, 64);
   };
 
-  const double pthr = double(top_p) * S_at(kk - 1);
-  int first = INT_MAX;
+  // first candidate (in lane-major order) meeting a cut: the first lane with a
+  // hit, then that lane's first hit
+  auto first_hit = [&](int lim, double thr, bool inclusive) {
+    int mine = INT_MAX;
 #pragma unroll
-  for (int j = P - 1; j >= 0; --j) {
-    const int i = lane * P + j;
-    if (i < kk && S[j] >= pthr) first = i;
-  }
-  first = wave_min_i32(first);
-  const int m = first == INT_MAX ? kk : first + 1;
+    for (int j = P - 1; j >= 0; --j) {
+      const int i = lane * P + j;
+      if (i < lim && (inclusive ? S[j] >= thr : S[j] > thr)) mine = i;
+    }
+    const uint64_t hits = __ballot(mine != INT_MAX);
+    return hits ? __shfl(mine, __ffsll((unsigned long long)hits) - 1, 64) : INT_MAX;
+  };
 
-  const double uthr = double(u) * S_at(m - 1);
-  first = INT_MAX;
-#pragma unroll
-  for (int j = P - 1; j >= 0; --j) {
-    const int i = lane * P + j;
-    if (i < m && S[j] > uthr) first = i;
-  }
-  first = wave_min_i32(first);
+  const int first_p = first_hit(kk, double(top_p) * S_at(kk - 1), true);
+  const int m = first_p == INT_MAX ? kk : first_p + 1;
+  const int first = first_hit(m, double(u) * S_at(m - 1), false);
   return ix[first == INT_MAX ? m - 1 : first];
 }
 

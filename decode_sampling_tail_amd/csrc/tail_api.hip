@@ -96,6 +96,32 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   return TAIL_OK;
 }
 
+// RMSNorm + lm_head: fused weight-streaming kernel, or RMSNorm then the
+// weight-streaming kernel, or the bf16-split producer then the matrix cores.
+// y (gbs*H floats) and act (split_geom bytes) are workspace.
+hipError_t norm_lm_head(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t,
+                        int gbs, int H, int H_u, int V, float eps, int ps, bool deferred, float* y,
+                        float* r, uint16_t* act, float* logits, uint32_t* gkey, hipStream_t st) {
+  const SplitGeom sg = split_geom(gbs, H, H_u, ps);
+  if (tail::gemv_fusable(gbs, sg.K))
+    return tail::launch_norm_gemv(hidden, dtype, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, w_t,
+                                  V, logits, r, gkey, st);
+  hipError_t e;
+  if (gbs <= tail::kGemvMaxBatch) {
+    e = tail::launch_rmsnorm(hidden, dtype, gamma, gbs, H, H_u, ps, eps, deferred, y, r, st);
+    if (e == hipSuccess)
+      e = tail::launch_lm_head_gemv(y, H, w_t, deferred ? r : nullptr, gbs, sg.K, ps, V, logits,
+                                    gkey, st);
+    return e;
+  }
+  e = tail::launch_split(hidden, dtype, true, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, sg.nt,
+                         sg.rows_pad, sg.Kp, act, r, st);
+  if (e == hipSuccess)
+    e = tail::launch_lm_head_mfma(act, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps, deferred ? r : nullptr,
+                                  gbs, logits, gkey, st);
+  return e;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? TAIL_OK : TAIL_ERR_HIP; }
 
 }  // namespace
@@ -167,6 +193,31 @@ TAIL_API int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_
   return hip_status(e);
 }
 
+TAIL_API int tail_rmsnorm_lm_head(const void* hidden, int dtype, const float* gamma,
+                                  const uint16_t* w_t, int gbs, int H, int H_u, int V, float eps,
+                                  unsigned flags, float* logits, float* out_r, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  if (int s = check_shape(gbs, H, H_u)) return s;
+  if (int s = check_vocab(V)) return s;
+  if (dtype != TAIL_F32 && dtype != TAIL_F16 && dtype != TAIL_BF16) return TAIL_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return TAIL_ERR_INVALID_ARG;
+  if (flags & ~(TAIL_EMIT_LOGITS | TAIL_ZERO_PAD | TAIL_DEFERRED_RMS)) return TAIL_ERR_INVALID_ARG;
+  const int ps = pad_stride(H, H_u, flags);
+  if (ps < 0) return TAIL_ERR_INVALID_ARG;
+  if (!hidden || !gamma || !w_t || !logits) return TAIL_ERR_INVALID_ARG;
+  if (!aligned(hidden, dtype_bytes(dtype)) || !aligned(gamma, 4) || !aligned(w_t, 16) ||
+      !aligned(logits, 16) || (out_r && !aligned(out_r, 4)))
+    return TAIL_ERR_INVALID_ARG;
+  // the same workspace layout as tail_forward (its y, r and act regions)
+  const FwdLayout L = forward_layout(gbs, H, H_u, ps, V, 1, flags | TAIL_EMIT_LOGITS);
+  if (int s = check_ws(ws, ws_bytes, L.gkey)) return s;
+  char* base = (char*)ws;
+  float* r = out_r ? out_r : (float*)(base + L.r);
+  return hip_status(norm_lm_head(hidden, dtype, gamma, w_t, gbs, H, H_u, V, eps, ps,
+                                 flags & TAIL_DEFERRED_RMS, (float*)(base + L.y), r,
+                                 (uint16_t*)(base + L.act), logits, nullptr, (hipStream_t)stream));
+}
+
 TAIL_API int tail_topk(const float* logits, int gbs, int V, int k, float* vals, int32_t* idx,
                        void* ws, size_t ws_bytes, void* stream) {
   if (gbs < 1) return TAIL_ERR_INVALID_ARG;
@@ -233,19 +284,8 @@ TAIL_API int tail_forward(const void* hidden, int dtype, const float* gamma, con
   // 64-column groups; otherwise from a separate pass over the logits
   const bool fused_groups = g.gs == tail::kFusedGroup;
   uint32_t* gk_fused = fused_groups ? gk : nullptr;
-  hipError_t e;
-  if (gbs <= tail::kGemvMaxBatch) {  // RMSNorm -> weight-streaming lm_head
-    e = tail::launch_rmsnorm(hidden, dtype, gamma, gbs, H, H_u, ps, eps, deferred, y, r, st);
-    if (e == hipSuccess)
-      e = tail::launch_lm_head_gemv(y, H, w_t, deferred ? r : nullptr, gbs, sg.K, ps, V, lg,
-                                    gk_fused, st);
-  } else {  // RMSNorm + bf16 split -> matrix-core lm_head
-    e = tail::launch_split(hidden, dtype, true, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, sg.nt,
-                           sg.rows_pad, sg.Kp, act, r, st);
-    if (e == hipSuccess)
-      e = tail::launch_lm_head_mfma(act, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
-                                    deferred ? r : nullptr, gbs, lg, gk_fused, st);
-  }
+  hipError_t e = norm_lm_head(hidden, dtype, gamma, w_t, gbs, H, H_u, V, eps, ps, deferred, y, r,
+                              act, lg, gk_fused, st);
   if (e == hipSuccess && !fused_groups) e = tail::launch_group_max(lg, gbs, V, g, gk, st);
   if (e == hipSuccess)
     e = tail::launch_select(lg, gbs, V, k, g, gk, vals, idx, params, ncols, tokens, st);

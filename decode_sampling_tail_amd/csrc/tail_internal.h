@@ -70,11 +70,19 @@ inline bool topk_geometry(int V, int k, TopkGeom* g) {
 hipError_t launch_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int H, int H_u,
                           int pad_s, float eps, bool deferred, float* y, float* r, hipStream_t st);
 
-// gkey (may be NULL): per row, the largest order-preserving key of each group
-// of kFusedGroup columns, [gbs, ceil(V / kFusedGroup)].
+// Weight-streaming lm_head over K contraction lanes (pad lanes skipped when
+// pad_s > 0).  gkey (may be NULL): per row, the largest order-preserving key
+// of each group of kFusedGroup columns, [gbs, ceil(V / kFusedGroup)].
 hipError_t launch_lm_head_gemv(const float* y, int ldy, const uint16_t* w, const float* row_scale,
-                               int gbs, int H_u, int pad_s, int V, float* logits, uint32_t* gkey,
+                               int gbs, int K, int pad_s, int V, float* logits, uint32_t* gkey,
                                hipStream_t st);
+
+// The same with the RMSNorm fused into the prologue (hidden rows in their
+// storage dtype); r_out (may be NULL) receives the per-row rms scale.
+bool gemv_fusable(int gbs, int K);
+hipError_t launch_norm_gemv(const void* hidden, int dtype, const float* gamma, int gbs, int H,
+                            int H_u, int K, int pad_s, float eps, bool deferred, const uint16_t* w,
+                            int V, float* logits, float* r_out, uint32_t* gkey, hipStream_t st);
 
 // Batches above this size run the lm_head on the matrix cores.
 constexpr int kGemvMaxBatch = 4;

@@ -8,10 +8,10 @@
 // inputs group_max_kernel computes them in one pass over the logits.
 //
 // select_kernel, one 1024-thread workgroup per row:
-//  a. t0 = the k-th largest group maximum (radix select, 8-bit digits).  At
-//     least k groups have a maximum >= t0 and each maximum is an element, so
-//     every top-k member is >= t0, and only groups whose maximum is >= t0 can
-//     hold one.
+//  a. t0 = a lower bound of the k-th largest group maximum (one histogram of
+//     the maxima in power-of-two bins).  At least k groups have a maximum >=
+//     t0 and each maximum is an element, so every top-k member is >= t0, and
+//     only groups whose maximum is >= t0 can hold one.
 //  b. Those groups are scanned (loads batched four deep per thread) and every
 //     element >= t0 is appended to an LDS list as the composite key
 //     (value key << 32) | ~index: larger value first, lower index first.
@@ -19,7 +19,8 @@
 //     and, when ties at v* would still leave more than 2k, to the lowest
 //     indices among the elements equal to v* (radix select on ~index).
 //  d. Each survivor's rank is the number of survivors with a larger composite
-//     key; ranks below k are written out (and kept in LDS for the sampler).
+//     key (up to 4 threads per survivor); ranks below k are written out (and
+//     kept in LDS for the sampler).
 //  e. More than kCap elements >= t0 (massive ties): the same two cuts are
 //     found by radix passes that re-read the candidate groups, then only the
 //     k winners are collected.  Exact for any input, slow only for such rows.
@@ -73,6 +74,7 @@ __global__ __launch_bounds__(kGmThreads) void group_max_kernel(const float* __re
 struct SelShared {
   uint32_t act[kMaxGroups];  // candidate groups of the row
   uint64_t c[kCap];          // candidate composite keys
+  uint32_t cb[kCap];         // their original value bits (keeps the sign of -0.0)
   float top_v[TAIL_K_MAX];   // the sorted result, for the sampler
   int32_t top_i[TAIL_K_MAX];
   uint32_t hist[256];
@@ -84,20 +86,67 @@ __device__ inline uint64_t composite(uint32_t key, int e) {
   return (uint64_t(key) << 32) | uint64_t(~uint32_t(e));
 }
 
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+__device__ inline uint32_t wave_sum_u32(uint32_t v) {
+  for (int off = 32; off >= 1; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, 64);
+  return v;
+}
+
 // Block-wide radix select: the k-th largest (k >= 1) 32-bit key among those
 // visit(f) enumerates (f(key) once per key of the calling thread; every
 // thread calls visit).  Returns the key; *above = keys strictly greater,
 // *equal = keys equal to it.  The visited set must hold at least k keys.
+// A first pass takes the keys' minimum and maximum, so the digit passes
+// (8 bits each, most significant first) start at the highest bit on which
+// the keys differ: no pass spends its histogram on one crowded bin.
 template <typename Visit>
 __device__ uint32_t radix_kth(SelShared& s, int tid, uint32_t k, Visit&& visit, uint32_t* above,
                               uint32_t* equal) {
-  uint32_t prefix = 0, need = k, eq = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+  uint32_t lo = 0xFFFFFFFFu, hi = 0, cnt = 0;
+  visit([&](uint32_t key) {
+    lo = min(lo, key);
+    hi = max(hi, key);
+    ++cnt;
+  });
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  cnt = wave_sum_u32(cnt);
+  if (tid == 0) {
+    s.bc[0] = 0xFFFFFFFFu;
+    s.bc[1] = 0u;
+    s.bc[2] = 0u;
+  }
+  __syncthreads();
+  if ((tid & 63) == 0) {
+    atomicMin(&s.bc[0], lo);
+    atomicMax(&s.bc[1], hi);
+    atomicAdd(&s.bc[2], cnt);
+  }
+  __syncthreads();
+  lo = s.bc[0];
+  hi = s.bc[1];
+  cnt = s.bc[2];
+  __syncthreads();
+  if (lo == hi) {  // all keys equal
+    *above = 0;
+    *equal = cnt;
+    return lo;
+  }
+  int top = 31 - __clz(int(lo ^ hi));  // highest bit on which keys differ
+  uint32_t prefix = top == 31 ? 0u : (hi & ~((2u << top) - 1u));
+  uint32_t need = k, eq = 0;
+  while (top >= 0) {
+    const int w = top + 1 < 8 ? top + 1 : 8;
+    const int shift = top - w + 1;
+    const uint32_t amask = top == 31 ? 0u : ~((2u << top) - 1u);  // bits above the digit
+    const uint32_t dmask = (1u << w) - 1u;
     if (tid < 256) s.hist[tid] = 0;
     __syncthreads();
     visit([&](uint32_t key) {
-      if ((key & hmask) == prefix) atomicAdd(&s.hist[(key >> shift) & 255u], 1u);
+      if ((key & amask) == prefix) atomicAdd(&s.hist[(key >> shift) & dmask], 1u);
     });
     __syncthreads();
     if (tid < 64) {  // wave 0: bins in descending digit order, lane l holds 255-4l .. 252-4l
@@ -127,6 +176,8 @@ __device__ uint32_t radix_kth(SelShared& s, int tid, uint32_t k, Visit&& visit, 
     prefix |= s.bc[0] << shift;
     need = s.bc[1];
     eq = s.bc[2];
+    top = shift - 1;
+    __syncthreads();
   }
   *above = k - need;
   *equal = eq;
@@ -135,7 +186,8 @@ __device__ uint32_t radix_kth(SelShared& s, int tid, uint32_t k, Visit&& visit, 
 
 // Append (key, e) of the lanes where pred holds; slots past kCap are counted
 // but not stored.  Must be called by all lanes of the wave.
-__device__ inline void wave_append(SelShared& s, bool pred, uint32_t key, int e, int lane) {
+__device__ inline void wave_append(SelShared& s, bool pred, uint32_t key, int e, uint32_t bits,
+                                   int lane) {
   const uint64_t mask = __ballot(pred);
   if (mask == 0) return;
   uint32_t base = 0;
@@ -143,7 +195,10 @@ __device__ inline void wave_append(SelShared& s, bool pred, uint32_t key, int e,
   base = (uint32_t)__shfl((int)base, 0, 64);
   if (pred) {
     const uint32_t pos = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-    if (pos < kCap) s.c[pos] = composite(key, e);
+    if (pos < kCap) {
+      s.c[pos] = composite(key, e);
+      s.cb[pos] = bits;
+    }
   }
 }
 
@@ -176,10 +231,10 @@ __device__ inline void for_candidates(const SelShared& s, const float* row, int 
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        f(in[u], float_key(v[u].x), e[u]);
-        f(in[u], float_key(v[u].y), e[u] + 1);
-        f(in[u], float_key(v[u].z), e[u] + 2);
-        f(in[u], float_key(v[u].w), e[u] + 3);
+        f(in[u], float_key(v[u].x), e[u], __float_as_uint(v[u].x));
+        f(in[u], float_key(v[u].y), e[u] + 1, __float_as_uint(v[u].y));
+        f(in[u], float_key(v[u].z), e[u] + 2, __float_as_uint(v[u].z));
+        f(in[u], float_key(v[u].w), e[u] + 3, __float_as_uint(v[u].w));
       }
     }
   } else {
@@ -192,7 +247,8 @@ __device__ inline void for_candidates(const SelShared& s, const float* row, int 
         e = int(s.act[fi / gs]) * gs + fi % gs;
         in = e < V;
       }
-      f(in, in ? float_key(row[e]) : 0u, e);
+      const float x = in ? row[e] : 0.0f;
+      f(in, float_key(x), e, __float_as_uint(x));
     }
   }
 }
@@ -208,19 +264,67 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const float* row = logits + size_t(row_id) * V;
   uint32_t above, equal;
 
-  // a. t0 = k-th largest group maximum
+  RowParams prm{0.f, 0.f, 0.f, 0.f};
+  if (params != nullptr && tid < 64) prm = load_params(params, ncols, row_id);
+
+  // a. t0: a lower bound of the k-th largest group maximum from one histogram
+  // of the group maxima over [lo, hi] in power-of-two bins: the bin where the
+  // count from the top first reaches k starts at t0, so at least k group
+  // maxima (hence k elements) are >= t0.
   uint32_t gk[kGPer];
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
   for (int j = 0; j < kGPer; ++j) {
     const int g = tid + j * kSelThreads;
     gk[j] = g < groups ? gkey[size_t(row_id) * groups + g] : 0u;
+    if (g < groups) {
+      lo = min(lo, gk[j]);
+      hi = max(hi, gk[j]);
+    }
   }
-  if (tid == 0) s.cnt = s.nact = 0;
-  const uint32_t t0 = radix_kth(s, tid, uint32_t(k), [&](auto&& f) {
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (tid < 256) s.hist[tid] = 0;
+  if (tid == 0) {
+    s.cnt = s.nact = 0;
+    s.bc[0] = 0xFFFFFFFFu;
+    s.bc[1] = 0u;
+  }
+  __syncthreads();
+  if (lane == 0) {
+    atomicMin(&s.bc[0], lo);
+    atomicMax(&s.bc[1], hi);
+  }
+  __syncthreads();
+  lo = s.bc[0];
+  hi = s.bc[1];
+  const uint32_t span = hi - lo;
+  const int bshift = span < 256u ? 0 : 32 - __clz(int(span >> 8));  // (span >> bshift) < 256
 #pragma unroll
-    for (int j = 0; j < kGPer; ++j)
-      if (tid + j * kSelThreads < groups) f(gk[j]);
-  }, &above, &equal);
+  for (int j = 0; j < kGPer; ++j)
+    if (tid + j * kSelThreads < groups) atomicAdd(&s.hist[(gk[j] - lo) >> bshift], 1u);
+  __syncthreads();
+  if (tid < 64) {  // wave 0: bins in descending order, lane l holds 255-4l .. 252-4l
+    uint32_t c[4], loc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = s.hist[255 - 4 * tid - j];
+      loc += c[j];
+    }
+    uint32_t incl = loc;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t t = (uint32_t)__shfl_up((int)incl, off, 64);
+      if (tid >= off) incl += t;
+    }
+    uint32_t run = incl - loc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (run < uint32_t(k) && run + c[j] >= uint32_t(k)) s.bc[2] = 255 - 4 * tid - j;
+      run += c[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t t0 = lo + (s.bc[2] << bshift);
 
   // list the candidate groups
 #pragma unroll
@@ -239,14 +343,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
   // b. every element >= t0
   for_candidates(s, row, V, gs, nact, tid,
-                 [&](bool in, uint32_t key, int e) { wave_append(s, in && key >= t0, key, e, lane); });
+                 [&](bool in, uint32_t key, int e, uint32_t bits) {
+                   wave_append(s, in && key >= t0, key, e, bits, lane);
+                 });
   __syncthreads();
   uint32_t n = s.cnt;
 
   // e. too many: find the cut by radix passes over the candidate groups
   if (n > uint32_t(kCap)) {
     auto visit_all = [&](auto&& f) {
-      for_candidates(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int) {
+      for_candidates(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int, uint32_t) {
         if (in && key >= t0) f(key);
       });
     };
@@ -255,7 +361,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (above + equal > uint32_t(kCap)) {
       uint32_t a2, e2;
       const uint32_t nk = radix_kth(s, tid, uint32_t(k) - above, [&](auto&& f) {
-        for_candidates(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int e) {
+        for_candidates(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int e, uint32_t) {
           if (in && key == vstar) f(~uint32_t(e));
         });
       }, &a2, &e2);
@@ -264,8 +370,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __syncthreads();
     if (tid == 0) s.cnt = 0;
     __syncthreads();
-    for_candidates(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int e) {
-      wave_append(s, in && (key > vstar || (key == vstar && e <= ecut)), key, e, lane);
+    for_candidates(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int e, uint32_t bits) {
+      wave_append(s, in && (key > vstar || (key == vstar && e <= ecut)), key, e, bits, lane);
     });
     __syncthreads();
     n = s.cnt;
@@ -274,10 +380,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // c. cut long lists to the k best (value, then lowest index among ties)
   if (n > uint32_t(2 * k)) {
     uint64_t mine[kPerThread];
+    uint32_t mbits[kPerThread];
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int i = tid + j * kSelThreads;
       mine[j] = i < int(n) ? s.c[i] : 0ull;
+      mbits[j] = i < int(n) ? s.cb[i] : 0u;
     }
     const uint32_t vstar = radix_kth(s, tid, uint32_t(k), [&](auto&& f) {
 #pragma unroll
@@ -305,35 +413,60 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         uint32_t base = 0;
         if (lane == 0) base = atomicAdd(&s.cnt, (uint32_t)__popcll(m));
         base = (uint32_t)__shfl((int)base, 0, 64);
-        if (keep) s.c[base + __popcll(m & ((1ull << lane) - 1ull))] = mine[j];
+        if (keep) {
+          const uint32_t pos = base + __popcll(m & ((1ull << lane) - 1ull));
+          s.c[pos] = mine[j];
+          s.cb[pos] = mbits[j];
+        }
       }
     }
     __syncthreads();
     n = s.cnt;
   }
 
-  // d. rank by composite key; the k best go out in order
-  for (int i = tid; i < int(n); i += kSelThreads) {
-    const uint64_t ci = s.c[i];
+  // d. rank by composite key; the k best go out in order.  TP threads share a
+  // candidate, each comparing it with every TP-th pair of the list; all lanes
+  // of a wave read the same few pairs at once (LDS broadcast).
+  if (n & 1) {  // pad to an even count with a key below every candidate
+    if (tid == 0) s.c[n] = 0ull;
+    __syncthreads();
+  }
+  const int n2 = int(n + 1) / 2;
+  const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(s.c);
+  const int TP = int(n) * 4 <= kSelThreads ? 4 : (int(n) * 2 <= kSelThreads ? 2 : 1);
+  for (int base = 0; base < int(n) * TP; base += kSelThreads) {
+    const int slot = base + tid;
+    const int i = slot / TP, q = slot % TP;
+    uint64_t ci = i < int(n) ? s.c[i] : ~0ull;
     uint32_t rank = 0;
-    for (int j = 0; j < int(n); ++j) rank += s.c[j] > ci;
-    if (rank < uint32_t(k)) {
-      const int e = int(~uint32_t(ci));
-      const float v = row[e];
-      vals[size_t(row_id) * k + rank] = v;
-      idx[size_t(row_id) * k + rank] = e;
-      s.top_v[rank] = v;
-      s.top_i[rank] = e;
+    int j = q;
+    for (; j + 3 * TP < n2; j += 4 * TP) {
+      const ulonglong2 a = c2[j], b = c2[j + TP], c = c2[j + 2 * TP], d = c2[j + 3 * TP];
+      rank += (a.x > ci) + (a.y > ci) + (b.x > ci) + (b.y > ci) + (c.x > ci) + (c.y > ci) +
+              (d.x > ci) + (d.y > ci);
+    }
+    for (; j < n2; j += TP) {
+      const ulonglong2 a = c2[j];
+      rank += (a.x > ci) + (a.y > ci);
+    }
+    for (int off = 1; off < TP; off <<= 1) rank += (uint32_t)__shfl_xor((int)rank, off, 64);
+    if (q == 0 && i < int(n) && rank < uint32_t(k)) {
+      s.top_v[rank] = __uint_as_float(s.cb[i]);
+      s.top_i[rank] = int(~uint32_t(ci));
     }
   }
+  __syncthreads();
 
-  // f. the row's sampler
-  if (params != nullptr) {
-    __syncthreads();
-    if (tid < 64) {
-      const RowParams p = load_params(params, ncols, row_id);
-      const int32_t t = sample_row_wave<P>(s.top_v, s.top_i, k, p.top_k, p.top_p, p.temp, p.u, lane);
-      if (lane == 0) tokens[row_id] = t;
+  // f. the row's sampler (wave 0) while the other waves write the list out
+  if (params != nullptr && tid < 64) {
+    const int32_t t = sample_row_wave<P>(s.top_v, s.top_i, k, prm.top_k, prm.top_p, prm.temp,
+                                         prm.u, lane);
+    if (lane == 0) tokens[row_id] = t;
+  }
+  for (int i = params != nullptr ? tid - 64 : tid; i < k; i += kSelThreads) {
+    if (i >= 0) {
+      vals[size_t(row_id) * k + i] = s.top_v[i];
+      idx[size_t(row_id) * k + i] = s.top_i[i];
     }
   }
 }

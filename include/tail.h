@@ -97,9 +97,12 @@ int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int
  *                      deferred rms scale), or NULL for none.
  *   logits    [gbs, V] fp32, 16-byte aligned:
  *                      logits[b,v] = row_scale[b] * sum_h y[b,h] * W[h,v],
- *                      the sum in fp32 over the real (non-pad) lanes with
- *                      full-precision fp32 activations (the activations are
- *                      never rounded to bf16).
+ *                      the sum in fp32 over the real (non-pad) lanes.  The
+ *                      activations are never rounded to a single bf16: the
+ *                      weight-streaming path (gbs <= 4) uses them as fp32;
+ *                      the matrix-core path splits each into bf16 terms
+ *                      whose sum keeps it to 2^-26 relative (3 terms, gbs <=
+ *                      64) or 2^-17 (2 terms, larger batches).
  *   ws, ws_bytes       workspace of at least tail_workspace_size() bytes,
  *                      256-byte aligned (may be NULL when that size is 0).
  * Only TAIL_ZERO_PAD is meaningful in `flags`.
@@ -107,6 +110,26 @@ int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int
 int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_scale, int gbs, int H,
                  int H_u, int V, unsigned flags, float* logits, void* ws, size_t ws_bytes,
                  void* stream);
+
+/*
+ * tail_rmsnorm_lm_head -- the final RMSNorm and the lm_head in one call
+ * ("hidden_states", "gamma", "eps", "hidden_actual", "zero_interleaved_pad",
+ * "deferred_rms", "lm_head_weight_t"): the logits of tail_rmsnorm followed by
+ * tail_lm_head, with the row's rms scale applied after the contraction under
+ * TAIL_DEFERRED_RMS (the page's default) or inside the activations without it.
+ * On small batches the normalization runs in the prologue of the
+ * weight-streaming kernel; on larger ones it writes the activations that the
+ * matrix-core kernel reads.
+ *
+ *   hidden, dtype, gamma, gbs, H, H_u, eps, w_t, V: as above.
+ *   logits [gbs, V] fp32, 16-byte aligned.
+ *   out_r  [gbs] fp32 or NULL: the per-row rms scale r.
+ *   ws, ws_bytes: workspace of at least tail_workspace_size() bytes.
+ * TAIL_ZERO_PAD and TAIL_DEFERRED_RMS are meaningful in `flags`.
+ */
+int tail_rmsnorm_lm_head(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t,
+                         int gbs, int H, int H_u, int V, float eps, unsigned flags, float* logits,
+                         float* out_r, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * tail_topk -- global top-k of every row over the full vocabulary ("k",
@@ -158,8 +181,9 @@ int tail_forward(const void* hidden, int dtype, const float* gamma, const uint16
                  size_t ws_bytes, void* stream);
 
 /*
- * Workspace bytes needed by tail_forward, tail_lm_head and tail_topk for these
- * sizes and flags (one buffer of this size serves any of them).  Returns 0
+ * Workspace bytes needed by tail_forward, tail_rmsnorm_lm_head, tail_lm_head
+ * and tail_topk for these sizes and flags (one buffer of this size serves any
+ * of them).  Returns 0
  * for arguments that the calls would reject.  Pure host function.
  */
 size_t tail_workspace_size(int gbs, int H, int H_u, int V, int k, unsigned flags);

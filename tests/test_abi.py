@@ -111,6 +111,32 @@ def test_lm_head_validation():
     assert lmh(flags=1 << 5) == E
 
 
+def rlh(**kw):
+    a = dict(hidden=P, dtype=dst.BF16, gamma=P, w=P, gbs=1, H=2880, H_u=2880, V=201088, eps=1e-5,
+             flags=dst.DEFERRED_RMS, logits=P, r=P, ws=P, ws_bytes=1 << 40)
+    a.update(kw)
+    return dst.lib().tail_rmsnorm_lm_head(a["hidden"], a["dtype"], a["gamma"], a["w"], a["gbs"],
+                                          a["H"], a["H_u"], a["V"], a["eps"], a["flags"],
+                                          a["logits"], a["r"], a["ws"], a["ws_bytes"], None)
+
+
+def test_rmsnorm_lm_head_validation():
+    E = dst.ERR_INVALID_ARG
+    assert rlh(hidden=NULL) == E
+    assert rlh(gamma=NULL) == E
+    assert rlh(w=NULL) == E
+    assert rlh(logits=NULL) == E
+    assert rlh(dtype=5) == E
+    assert rlh(eps=-1.0) == E
+    assert rlh(H_u=2881) == E
+    assert rlh(gbs=0) == E
+    assert rlh(flags=16) == E
+    assert rlh(w=ctypes.c_void_p(0x100008)) == E
+    assert rlh(V=100) == dst.ERR_UNSUPPORTED
+    assert rlh(ws=NULL) == dst.ERR_WORKSPACE
+    assert rlh(gbs=64, ws_bytes=1024) == dst.ERR_WORKSPACE   # matrix-core activations need room
+
+
 def tk(**kw):
     a = dict(logits=P, gbs=2, V=4096, k=16, vals=P, idx=P, ws=P, ws_bytes=1 << 20)
     a.update(kw)

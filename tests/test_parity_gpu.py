@@ -88,6 +88,38 @@ def test_lm_head(gbs, H, H_u, V, zp):
     assert np.all(np.isfinite(L))
 
 
+@pytest.mark.parametrize("gbs,H,H_u,V,zp,dtype,deferred", [
+    (1, 2880, 2880, 4096, False, synth.DT_BF16, True), (1, 2880, 2880, 4096, False, synth.DT_BF16, False),
+    (3, 3072, 2880, 2056, True, synth.DT_F16, True), (4, 300, 300, 1160, False, synth.DT_F32, False),
+    (8, 640, 640, 2048, False, synth.DT_F32, True), (40, 3072, 2880, 1032, True, synth.DT_F16, False),
+    (130, 256, 256, 520, False, synth.DT_BF16, True)])
+def test_rmsnorm_lm_head(gbs, H, H_u, V, zp, dtype, deferred):
+    rng = np.random.default_rng(V * 3 + gbs)
+    pad = oracle.pad_mask(H, H_u, zp)
+    x = (rng.standard_normal((gbs, H)) * rng.uniform(0.1, 10, (gbs, 1))).astype(np.float32)
+    x[:, pad] = np.nan if zp else 0.0
+    gamma = (1 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    gamma[pad] = np.nan if zp else gamma[pad]
+    w = bf16_bits(rng.standard_normal((H, V)) * 0.02)
+    w[pad] = 0x7FC0 if zp else 0
+    if dtype == synth.DT_F16:
+        xs = x.astype(np.float16)
+        xt = torch.from_numpy(xs).cuda()
+    elif dtype == synth.DT_BF16:
+        xs = synth.round_bf16(x)
+        xt = gpu_bf16(xs)
+    else:
+        xs = x
+        xt = torch.from_numpy(x).cuda()
+    L, r = dst.rmsnorm_lm_head(xt, torch.from_numpy(gamma).cuda(), gpu_bf16(w), H_u, 1e-5, zp, deferred)
+    L, r = np_(L), np_(r).astype(np.float64)
+    y, rr = oracle.rmsnorm(oracle.widen(xs, dtype), gamma, H_u, 1e-5, pad)
+    ref = oracle.logits(y, w, pad)
+    assert np.all(np.abs(r - rr) <= 2e-7 * rr)
+    fails, rel, mx = check_logits(L, ref)
+    assert not fails, fails
+
+
 @pytest.mark.parametrize("big", [4, 40])
 def test_lm_head_duplicate_columns_and_batch_invariance(big):
     """Duplicated weight columns give bitwise-equal logits wherever they sit, and
