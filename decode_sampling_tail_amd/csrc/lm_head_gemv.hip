@@ -41,15 +41,6 @@ constexpr int kMaxNB = 8;   // batch rows per pass
 constexpr int kWaves = 4;
 constexpr int kUnroll = 6;
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// The weight is streamed once and never reused: non-temporal loads keep it
-// from displacing useful lines and measurably raise the achieved bandwidth.
-__device__ inline uint4 load_stream(const uint16_t* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -12,18 +12,19 @@
 //
 // Tiling: a workgroup owns VT consecutive vocabulary columns for BROWS =
 // 16 * NBT batch rows and walks the (unpadded) hidden dimension in K-steps
-// of 64.  Per K-step the weight tile [64 x VT] is staged into LDS in its
-// natural row-major form and each 16-column MFMA operand is read back with
-// two ds_read_b64_tr_b16 transposing reads; the activation tile [BROWS x 64]
-// per term is staged next to it.  Loads of the next K-step go out (weight
-// loads non-temporal) before the current step's MFMAs.  Waves form a WV x WB
-// grid over (columns, rows); each wave owns (VT/WV) x (BROWS/WB) outputs.
+// of KT (32 or 64) rows.  Per K-step the weight tile [KT x VT] is staged into
+// LDS in its natural row-major form (row pitch 2 VT + 16 bytes) and each
+// 16-column MFMA operand is read back with two ds_read_b64_tr_b16
+// transposing reads; the activation tile [BROWS x KT] per term is staged next
+// to it.  Loads of the next K-step go out (weight loads non-temporal) before
+// the current step's MFMAs.  Waves form a WV x WB grid over (columns, rows);
+// each wave owns (VT/WV) x (BROWS/WB) outputs.
 //
 // K order inside a 32-lane block: MFMA k-slot (g, j) (lane group g, element
-// j) maps to block row 4g + (j & 3) + 16 (j >> 2), so the 16 lanes of a
-// transposing read touch 16 consecutive LDS rows (bank-conflict free with a
-// 528-byte row pitch).  The activation producer writes its terms in the same
-// permuted order, so both operands agree on every k.
+// j) maps to block row 4g + (j & 3) + 16 (j >> 2), so one transposing read
+// of the wave touches 16 consecutive LDS rows, 32 bytes of each.  The
+// activation producer writes its terms in the same permuted order, so both
+// operands agree on every k.
 //
 // Determinism: every output element is one fixed sequence of MFMAs (K-steps
 // in order, terms in order), the same for every column and every row.
@@ -35,28 +36,23 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int KT = 64;
-
-template <int VT, int WV, int WB, int NBT, int NT>
+template <int VT, int WV, int WB, int NBT, int NT, int KT>
 struct Cfg {
   static constexpr int NW = WV * WB, NTH = NW * 64;
   static constexpr int VW = VT / WV, VTW = VW / 16;            // columns, 16-col tiles per wave
   static constexpr int BROWS = NBT * 16, BW = BROWS / WB, BTW = BW / 16;
   static constexpr int WROW = VT * 2 + 16;                     // LDS bytes per weight row
   static constexpr int BROW = KT * 2 + 16;                     // LDS bytes per activation row
+  static constexpr int HCH = KT / 8;                           // 16-byte chunks per activation row
   static constexpr int WCH = KT * VT / 8, WPT = WCH / NTH;     // 16-byte weight chunks
   static constexpr int BCH = NT * BROWS * KT / 8, BPT = (BCH + NTH - 1) / NTH;
   static constexpr int GPW = VT / kFusedGroup;                 // key groups per workgroup
-  static_assert(WCH % NTH == 0 && VW % 16 == 0 && BW % 16 == 0 && VT % kFusedGroup == 0, "tile");
+  static_assert(WCH % NTH == 0 && VW % 16 == 0 && BW % 16 == 0 && VT % kFusedGroup == 0 &&
+                    kKStep % KT == 0 && KT % 32 == 0,
+                "tile");
 };
-
-__device__ inline uint4 load_stream(const uint16_t* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 __device__ inline bf16x8 tr_operand(const unsigned char* s_w, int row, int col_bytes, int wrow) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -68,12 +64,12 @@ __device__ inline bf16x8 tr_operand(const unsigned char* s_w, int row, int col_b
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int VT, int WV, int WB, int NBT, int NT>
+template <int VT, int WV, int WB, int NBT, int NT, int KT = 64>
 __global__ __launch_bounds__(WV * WB * 64) void mfma_kernel(
     const uint16_t* __restrict__ act, int rows_pad, int Kp, const uint16_t* __restrict__ w, int V,
     int H_u, int pad_s, FastDiv pdiv, const float* __restrict__ row_scale, int gbs, int b0,
     float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups) {
-  using C = Cfg<VT, WV, WB, NBT, NT>;
+  using C = Cfg<VT, WV, WB, NBT, NT, KT>;
   __shared__ __align__(16) unsigned char s_w[KT * C::WROW];
   __shared__ __align__(16) unsigned char s_b[NT * C::BROWS * C::BROW];
   __shared__ uint32_t s_g[C::BROWS][C::GPW];
@@ -82,7 +78,7 @@ __global__ __launch_bounds__(WV * WB * 64) void mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave % WV, wb = wave / WV;
   const int v0 = blockIdx.x * VT;
-  const int nks = Kp / KT;
+  const int nks = Kp / KT;  // Kp is a multiple of kKStep, which KT divides
 
   for (int i = tid; i < C::BROWS * C::GPW; i += C::NTH) (&s_g[0][0])[i] = 0u;
 
@@ -105,7 +101,8 @@ __global__ __launch_bounds__(WV * WB * 64) void mfma_kernel(
       const int c = tid + i * C::NTH;
       breg[i] = make_uint4(0, 0, 0, 0);
       if (c < C::BCH) {
-        const int t = c / (C::BROWS * 8), rem = c % (C::BROWS * 8), b = rem / 8, hc = rem % 8;
+        const int t = c / (C::BROWS * C::HCH), rem = c % (C::BROWS * C::HCH);
+        const int b = rem / C::HCH, hc = rem % C::HCH;
         const int row = b0 + b;
         if (row < rows_pad)
           breg[i] = *reinterpret_cast<const uint4*>(act + (size_t(t) * rows_pad + row) * Kp +
@@ -123,7 +120,8 @@ __global__ __launch_bounds__(WV * WB * 64) void mfma_kernel(
     for (int i = 0; i < C::BPT; ++i) {
       const int c = tid + i * C::NTH;
       if (c < C::BCH) {
-        const int t = c / (C::BROWS * 8), rem = c % (C::BROWS * 8), b = rem / 8, hc = rem % 8;
+        const int t = c / (C::BROWS * C::HCH), rem = c % (C::BROWS * C::HCH);
+        const int b = rem / C::HCH, hc = rem % C::HCH;
         *reinterpret_cast<uint4*>(s_b + (t * C::BROWS + b) * C::BROW + hc * 16) = breg[i];
       }
     }
@@ -204,14 +202,14 @@ __global__ __launch_bounds__(WV * WB * 64) void mfma_kernel(
   }
 }
 
-template <int VT, int WV, int WB, int NBT, int NT>
+template <int VT, int WV, int WB, int NBT, int NT, int KT = 64>
 hipError_t launch_cfg(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V, int H_u,
                       int pad_s, const float* row_scale, int gbs, int b0, float* logits,
                       uint32_t* gkey, hipStream_t st) {
   const FastDiv pdiv = make_fastdiv(pad_s > 1 ? uint32_t(pad_s - 1) : 1u);
   const int groups = (V + kFusedGroup - 1) / kFusedGroup;
   dim3 grid((V + VT - 1) / VT), block(WV * WB * 64);
-  hipLaunchKernelGGL((mfma_kernel<VT, WV, WB, NBT, NT>), grid, block, 0, st, act, rows_pad, Kp, w, V,
+  hipLaunchKernelGGL((mfma_kernel<VT, WV, WB, NBT, NT, KT>), grid, block, 0, st, act, rows_pad, Kp, w, V,
                      H_u, pad_s, pdiv, row_scale, gbs, b0, logits, gkey, groups);
   return hipGetLastError();
 }
@@ -229,9 +227,11 @@ hipError_t launch_lm_head_mfma(const uint16_t* act, int rows_pad, int Kp, const 
     const int nbt = (rows + 15) / 16;
     hipError_t e;
     if (nt == 3) {
-      if (nbt <= 1) e = launch_cfg<256, 4, 1, 1, 3>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else if (nbt <= 2) e = launch_cfg<256, 4, 1, 2, 3>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else e = launch_cfg<256, 2, 2, 4, 3>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      // 512-column tiles (393 workgroups for GPT-OSS, all resident at once)
+      // and 32-row K-steps: about 32 KB of weight loads in flight per workgroup
+      if (nbt <= 1) e = launch_cfg<512, 4, 1, 1, 3, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      else if (nbt <= 2) e = launch_cfg<512, 4, 2, 2, 3, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      else e = launch_cfg<512, 4, 2, 4, 3, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
     } else {
       if (nbt <= 8) e = launch_cfg<256, 2, 4, 8, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
       else e = launch_cfg<256, 2, 4, 16, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
