@@ -13,12 +13,15 @@
 // Tiling: a workgroup owns VT consecutive vocabulary columns for BROWS =
 // 16 * NBT batch rows and walks the (unpadded) hidden dimension in K-steps
 // of KT (32 or 64) rows.  Per K-step the weight tile [KT x VT] is staged into
-// LDS in its natural row-major form (row pitch 2 VT + 16 bytes) and each
+// LDS in its natural row-major form (row pitch 2 VT + 32 bytes) and each
 // 16-column MFMA operand is read back with two ds_read_b64_tr_b16
 // transposing reads; the activation tile [BROWS x KT] per term is staged next
-// to it.  Loads of the next K-step go out (weight loads non-temporal) before
-// the current step's MFMAs.  Waves form a WV x WB grid over (columns, rows);
-// each wave owns (VT/WV) x (BROWS/WB) outputs.
+// to it as the ready MFMA fragments the activation producer wrote (1 KB
+// each, lane l's 16 bytes at 16 l), so its global loads, LDS stores and LDS
+// reads are all linear, and the LDS accesses free of bank conflicts.
+// Loads of the next K-step go out (weight loads non-temporal) before the
+// current step's MFMAs.  Waves form a WV x WB grid over (columns, rows); each
+// wave owns (VT/WV) x (BROWS/WB) outputs.
 //
 // K order inside a 32-lane block: MFMA k-slot (g, j) (lane group g, element
 // j) maps to block row 4g + (j & 3) + 16 (j >> 2), so one transposing read
@@ -43,9 +46,8 @@ struct Cfg {
   static constexpr int NW = WV * WB, NTH = NW * 64;
   static constexpr int VW = VT / WV, VTW = VW / 16;            // columns, 16-col tiles per wave
   static constexpr int BROWS = NBT * 16, BW = BROWS / WB, BTW = BW / 16;
-  static constexpr int WROW = VT * 2 + 16;                     // LDS bytes per weight row
-  static constexpr int BROW = KT * 2 + 16;                     // LDS bytes per activation row
-  static constexpr int HCH = KT / 8;                           // 16-byte chunks per activation row
+  static constexpr int WROW = VT * 2 + 32;                     // LDS bytes per weight row
+  static constexpr int KB = KT / 32;                           // 32-lane K blocks per K-step
   static constexpr int WCH = KT * VT / 8, WPT = WCH / NTH;     // 16-byte weight chunks
   static constexpr int BCH = NT * BROWS * KT / 8, BPT = (BCH + NTH - 1) / NTH;
   static constexpr int GPW = VT / kFusedGroup;                 // key groups per workgroup
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(WV * WB * 64) void mfma_kernel(
     float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups) {
   using C = Cfg<VT, WV, WB, NBT, NT, KT>;
   __shared__ __align__(16) unsigned char s_w[KT * C::WROW];
-  __shared__ __align__(16) unsigned char s_b[NT * C::BROWS * C::BROW];
+  __shared__ __align__(16) unsigned char s_b[NT * C::BROWS * KT * 2];
   __shared__ uint32_t s_g[C::BROWS][C::GPW];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -101,12 +103,14 @@ __global__ __launch_bounds__(WV * WB * 64) void mfma_kernel(
       const int c = tid + i * C::NTH;
       breg[i] = make_uint4(0, 0, 0, 0);
       if (c < C::BCH) {
-        const int t = c / (C::BROWS * C::HCH), rem = c % (C::BROWS * C::HCH);
-        const int b = rem / C::HCH, hc = rem % C::HCH;
-        const int row = b0 + b;
-        if (row < rows_pad)
-          breg[i] = *reinterpret_cast<const uint4*>(act + (size_t(t) * rows_pad + row) * Kp +
-                                                    ks * KT + hc * 8);
+        // chunk c = ((t * NBT + bt) * KB + sb) * 64 + l: lane l of the fragment
+        // (term t, row tile b0 / 16 + bt, K block ks * KB + sb)
+        const int l = c % 64, sb = (c / 64) % C::KB, bt = (c / (64 * C::KB)) % NBT;
+        const int t = c / (64 * C::KB * NBT);
+        const int rt = b0 / 16 + bt;
+        if (rt < rows_pad / 16)
+          breg[i] = *reinterpret_cast<const uint4*>(
+              act + (((size_t(t) * (rows_pad / 16) + rt) * (Kp / 32) + ks * C::KB + sb) * 64 + l) * 8);
       }
     }
   };
@@ -119,11 +123,8 @@ __global__ __launch_bounds__(WV * WB * 64) void mfma_kernel(
 #pragma unroll
     for (int i = 0; i < C::BPT; ++i) {
       const int c = tid + i * C::NTH;
-      if (c < C::BCH) {
-        const int t = c / (C::BROWS * C::HCH), rem = c % (C::BROWS * C::HCH);
-        const int b = rem / C::HCH, hc = rem % C::HCH;
-        *reinterpret_cast<uint4*>(s_b + (t * C::BROWS + b) * C::BROW + hc * 16) = breg[i];
-      }
+      // fragment layout: chunk c is lane (c % 64) of fragment (t, bt, K block) c / 64
+      if (c < C::BCH) *reinterpret_cast<uint4*>(s_b + c * 16) = breg[i];
     }
   };
 
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(WV * WB * 64) void mfma_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           bfr[bt][t] = *reinterpret_cast<const bf16x8*>(
-              s_b + (t * C::BROWS + wb * C::BW + bt * 16 + s16) * C::BROW + (sb * 32 + 8 * kg) * 2);
+              s_b + (((t * NBT + wb * C::BTW + bt) * C::KB + sb) * 64 + lane) * 16);
 #pragma unroll
       for (int vt = 0; vt < C::VTW; ++vt) {
         const bf16x8 a = tr_operand(s_w, sb * 32 + tr_row, tr_col + vt * 32, C::WROW);
@@ -202,6 +203,240 @@ __global__ __launch_bounds__(WV * WB * 64) void mfma_kernel(
   }
 }
 
+// Persistent form for batches above 64 rows, with direct global-to-LDS copies
+// (global_load_lds_dwordx4) and a three-stage LDS ring.
+//
+// The grid holds as many workgroups as fit on the device at once; workgroup
+// w owns the contiguous range of 64-column key groups [w G / P, (w + 1) G / P)
+// (G groups, P workgroups), so every workgroup gets the same number of
+// columns to within one group, and walks it in sub-tiles of VT columns (the
+// last one may be narrower), one K-step of 32 rows at a time.  The K-steps of
+// all its sub-tiles form one pipeline: the copies for step q + 2 go out while
+// step q runs, without passing through registers, so two steps of memory
+// latency are hidden; one barrier per step.  Wave (wv, wb) owns tiles
+// wv * VTW .. wv * VTW + VTW - 1 (16 columns each) of the sub-tile for rows
+// (wb * BTW .. wb * BTW + BTW - 1) * 16 of the 16 * NBT-row chunk.  A
+// sub-tile's logits and its 64-column group maxima are written from the
+// accumulators, without a barrier, after its last K-step.
+//
+// Weight stage: the [32 x VT] tile is stored unpadded (row pitch 2 VT bytes)
+// with the 16-byte chunks of row r XOR-swizzled by 2 (r % 8); each copy moves
+// 1 KB (1024 / (2 VT) whole rows), lane l fetching the global chunk that
+// belongs in its LDS slot.  The transposing reads of half a wave touch rows
+// with distinct r % 8, which the swizzle spreads over distinct 32-byte bank
+// groups.  Activation stage: the 1 KB fragments of the step, one copy each.
+//
+// Rows past K and columns past V are fetched from clamped (valid) addresses:
+// a clamped weight row meets zero activations, and clamped columns or row
+// tiles only reach outputs that are never stored.
+template <int VT, int WV, int WB, int NBT, int NT>
+struct DCfg {
+  static constexpr int NW = WV * WB, NTH = NW * 64;
+  static constexpr int VTW = VT / 16 / WV, BTW = NBT / WB;
+  static constexpr int WPITCH = VT * 2, WBYTES = 32 * WPITCH;
+  static constexpr int WINS = WBYTES / 1024, RPI = 1024 / WPITCH;  // weight copies, rows per copy
+  static constexpr int BINS = NT * NBT, NINS = WINS + BINS;        // copies per step
+  static constexpr int WAIT = NINS / NW;                           // fewest copies of any wave
+  static constexpr int STAGE = WBYTES + BINS * 1024;
+  static_assert(VTW * 16 * WV == VT && VTW % 4 == 0 && BTW * WB == NBT && WPITCH <= 1024 &&
+                    VT >= 128 && (VT & (VT - 1)) == 0 && WAIT >= 1 && WAIT < 64 &&
+                    3 * STAGE <= 160 * 1024,
+                "tile");
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  // vmcnt field split over bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int VT, int WV, int WB, int NBT, int NT>
+__global__ __launch_bounds__(WV * WB * 64) void dma_kernel(
+    const uint16_t* __restrict__ act, int rows_pad, int Kp, const uint16_t* __restrict__ w, int V,
+    int K, int pad_s, FastDiv pdiv, const float* __restrict__ row_scale, int gbs, int b0,
+    float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups) {
+  using C = DCfg<VT, WV, WB, NBT, NT>;
+  __shared__ __align__(1024) unsigned char smem[3 * C::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = wave % WV, wb = wave / WV;
+  const int s16 = lane & 15, kg = lane >> 4;
+  const int P = gridDim.x;
+  const int g0 = int((long long)blockIdx.x * groups / P);
+  const int g1 = int((long long)(blockIdx.x + 1) * groups / P);
+  const int c0 = g0 * kFusedGroup, c1 = min(g1 * kFusedGroup, V);
+  const int nsub = (c1 - c0 + VT - 1) / VT;
+  const int nks = Kp / 32;
+  const int total = nsub * nks;
+  if (total <= 0) return;
+  const int rtiles = rows_pad / 16;
+
+  // this wave's copies of step q into stage (q % 3)
+  auto issue = [&](int q) {
+    const int j = q / nks, ks = q % nks;
+    const int v0 = c0 + j * VT;
+    unsigned char* st = smem + (q % 3) * C::STAGE;
+    for (int i = wave; i < C::NINS; i += C::NW) {
+      if (i < C::WINS) {
+        const int r = i * C::RPI + lane / (64 / C::RPI);
+        const int p = lane % (64 / C::RPI);
+        const int c = p ^ (2 * (r & 7));
+        const int u = min(ks * 32 + r, K - 1);
+        const int h = pad_s ? u + int(fastdiv(uint32_t(u), pdiv)) : u;
+        const int col = min(v0 + c * 8, V - 8);
+        __builtin_amdgcn_global_load_lds(w + size_t(h) * V + col, (lds_void*)(st + i * 1024), 16, 0,
+                                         2 /* non-temporal */);
+      } else {
+        const int f = i - C::WINS, t = f / NBT, bt = f % NBT;
+        const int rt = min(b0 / 16 + bt, rtiles - 1);
+        __builtin_amdgcn_global_load_lds(
+            act + (((size_t(t) * rtiles + rt) * (Kp / 32) + ks) * 64 + lane) * 8,
+            (lds_void*)(st + C::WBYTES + f * 1024), 16, 0, 0);
+      }
+    }
+  };
+
+  f32x4 acc[C::VTW][C::BTW];
+#pragma unroll
+  for (int i = 0; i < C::VTW; ++i)
+#pragma unroll
+    for (int j = 0; j < C::BTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // per-row output scales, loaded once (a load in the epilogue would make the
+  // compiler drain the copies in flight)
+  float scale[C::BTW];
+#pragma unroll
+  for (int bt = 0; bt < C::BTW; ++bt) {
+    const int b = b0 + (wb * C::BTW + bt) * 16 + s16;
+    scale[bt] = (b < gbs && row_scale) ? row_scale[b] : 1.0f;
+  }
+
+  // Transposing reads: lane (g, s) supplies row r = 4 g + (s >> 2) of the
+  // block (+16 for the second read) and bytes 8 (s & 3) .. +7 of the tile's
+  // 32-byte column pair, whose chunks sit at (2 tile) ^ (2 (r % 8)).  They are
+  // issued as inline assembly: the compiler cannot tell them apart from the
+  // LDS the copies in flight are filling and would wait for every copy.
+  const int tr_row = 4 * kg + (s16 >> 2);
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  const uint32_t smem_base = uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)smem));
+  uint32_t tr_addr[C::VTW];
+#pragma unroll
+  for (int vt = 0; vt < C::VTW; ++vt) {
+    const int tile = wv * C::VTW + vt;
+    const int ch = 2 * ((tile & ~7) | ((tile & 7) ^ (tr_row & 7)));
+    tr_addr[vt] = smem_base + tr_row * C::WPITCH + ch * 16 + 8 * (s16 & 3);
+  }
+
+  issue(0);
+  if (total > 1) issue(1);
+  for (int q = 0; q < total; ++q) {
+    // this wave's copies of step q are done once at most those of step q + 1
+    // are outstanding; the barrier extends that to every wave, and also
+    // retires every wave's reads of step q - 1, whose stage step q + 2 reuses
+    if (q + 1 < total) wait_vmcnt<C::WAIT>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (q + 2 < total) issue(q + 2);
+
+    const int j = q / nks, ks = q % nks;
+    const int v0 = c0 + j * VT, vend = min(v0 + VT, c1);
+    const int ntile = __builtin_amdgcn_readfirstlane((vend - v0 + 15) / 16 - wv * C::VTW);
+    const uint32_t soff = uint32_t((q % 3) * C::STAGE);
+    const unsigned char* st = smem + (q % 3) * C::STAGE;
+    s16x4 alo[C::VTW], ahi[C::VTW];
+#pragma unroll
+    for (int vt = 0; vt < C::VTW; ++vt) {
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(alo[vt]) : "v"(tr_addr[vt] + soff));
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                   : "=v"(ahi[vt])
+                   : "v"(tr_addr[vt] + soff), "i"(16 * C::WPITCH));
+    }
+    bf16x8 bfr[C::BTW][NT];
+#pragma unroll
+    for (int bt = 0; bt < C::BTW; ++bt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        bfr[bt][t] = *reinterpret_cast<const bf16x8*>(
+            st + C::WBYTES + ((t * NBT + wb * C::BTW + bt) * 64 + lane) * 16);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int vt = 0; vt < C::VTW; ++vt) asm volatile("" : "+v"(alo[vt]), "+v"(ahi[vt]));
+#pragma unroll
+    for (int vt = 0; vt < C::VTW; ++vt) {
+      if (vt < ntile) {
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 av = {alo[vt][0], alo[vt][1], alo[vt][2], alo[vt][3],
+                          ahi[vt][0], ahi[vt][1], ahi[vt][2], ahi[vt][3]};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+        for (int bt = 0; bt < C::BTW; ++bt)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[vt][bt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr[bt][t], acc[vt][bt], 0, 0, 0);
+      }
+    }
+    asm volatile("" ::: "memory");
+    if (ks == nks - 1) {
+#pragma unroll
+      for (int bt = 0; bt < C::BTW; ++bt) {
+        const int b = b0 + (wb * C::BTW + bt) * 16 + s16;
+        const float sc = scale[bt];
+        uint32_t gm = 0;
+#pragma unroll
+        for (int vt = 0; vt < C::VTW; ++vt) {
+          const int v = v0 + (wv * C::VTW + vt) * 16 + 4 * kg;
+          const float4 o = make_float4(acc[vt][bt][0] * sc, acc[vt][bt][1] * sc,
+                                       acc[vt][bt][2] * sc, acc[vt][bt][3] * sc);
+          if (b < gbs && v < vend) {
+            *reinterpret_cast<float4*>(logits + size_t(b) * V + v) = o;
+            gm = max(gm, max(max(float_key(o.x), float_key(o.y)),
+                             max(float_key(o.z), float_key(o.w))));
+          }
+          if (vt % 4 == 3) {
+            gm = max(gm, (uint32_t)__shfl_xor((int)gm, 16, 64));
+            gm = max(gm, (uint32_t)__shfl_xor((int)gm, 32, 64));
+            const int g = (v0 + (wv * C::VTW + vt - 3) * 16) / kFusedGroup;
+            if (gkey && kg == 0 && b < gbs && g < g1) gkey[size_t(b) * groups + g] = gm;
+            gm = 0;
+          }
+          acc[vt][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+  }
+}
+
+template <int VT, int WV, int WB, int NBT, int NT>
+hipError_t launch_dma(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V, int K,
+                      int pad_s, const float* row_scale, int gbs, int b0, float* logits,
+                      uint32_t* gkey, hipStream_t st) {
+  auto kern = dma_kernel<VT, WV, WB, NBT, NT>;
+  static int per_cu = -1;
+  if (per_cu < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, WV * WB * 64, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  const FastDiv pdiv = make_fastdiv(pad_s > 1 ? uint32_t(pad_s - 1) : 1u);
+  const int groups = (V + kFusedGroup - 1) / kFusedGroup;
+  const int P = min(groups, cus * per_cu);
+  hipLaunchKernelGGL(kern, dim3(P), dim3(WV * WB * 64), 0, st, act, rows_pad, Kp, w, V, K, pad_s,
+                     pdiv, row_scale, gbs, b0, logits, gkey, groups);
+  return hipGetLastError();
+}
+
 template <int VT, int WV, int WB, int NBT, int NT, int KT = 64>
 hipError_t launch_cfg(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V, int H_u,
                       int pad_s, const float* row_scale, int gbs, int b0, float* logits,
@@ -233,8 +468,9 @@ hipError_t launch_lm_head_mfma(const uint16_t* act, int rows_pad, int Kp, const 
       else if (nbt <= 2) e = launch_cfg<512, 4, 2, 2, 3, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
       else e = launch_cfg<512, 4, 2, 4, 3, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
     } else {
-      if (nbt <= 8) e = launch_cfg<256, 2, 4, 8, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else e = launch_cfg<256, 2, 4, 16, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      // persistent, direct-copy kernel; rows past the chunk are never stored
+      if (nbt <= 8) e = launch_dma<256, 2, 4, 8, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      else e = launch_dma<256, 2, 4, 16, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
     }
     if (e != hipSuccess) return e;
   }

@@ -103,19 +103,21 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restric
 // is taken over the real lanes only (compacted: unpadded index u), zero-padded
 // to Kp, and split into NT bf16 terms t_0 = bf16(y), t_1 = bf16(y - t_0),
 // t_2 = bf16(y - t_0 - t_1) (round to nearest even; each difference is exact
-// in fp32).  Inside each block of 32 lanes, unpadded lane 32 q + c is stored
-// at slot 32 q + p with c = 4 (p / 8 % 4) + (p % 4) + 16 (p % 8 / 4): the K
-// order of the matrix-core kernel's operands.
+// in fp32).
+//
+// Output layout: ready operand fragments of v_mfma_f32_16x16x32_bf16.  For
+// term t, row tile rt (rows 16 rt .. 16 rt + 15) and K block kb (unpadded
+// lanes 32 kb .. 32 kb + 31) one 1 KB fragment holds 64 lanes x 8 bf16; lane
+// 16 g + s carries row 16 rt + s at K slots 8 g .. 8 g + 7, and K slot
+// 8 g + j is unpadded lane 32 kb + 4 g + (j & 3) + 16 (j >> 2).  Fragments are
+// ordered (t, rt, kb), so the fragments of one row tile for consecutive K
+// blocks are contiguous.  Each thread produces one 16-byte lane (an "octet")
+// per term.
 __device__ inline uint16_t bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 __device__ inline float bf16_val(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
-
-__device__ inline int k_slot(int u) {
-  const int c = u & 31;
-  return (u & ~31) | (8 * ((c & 15) >> 2) + 4 * (c >> 4) + (c & 3));
-}
 
 template <int DT, int NT, bool NORM>
 __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict__ src,
@@ -128,10 +130,16 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
   __shared__ double s_part[kThreads / 64];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  const int nkb = Kp / 32, nrt = rows_pad / 16;
+  // 16-byte lane of octet o = 4 kb + g for term t
+  auto lane_ptr = [&](int t, int o) {
+    const size_t frag = (size_t(t) * nrt + row / 16) * nkb + o / 4;
+    return reinterpret_cast<uint4*>(act + (frag * 64 + (o % 4) * 16 + row % 16) * 8);
+  };
   if (row >= gbs) {
-    for (int i = tid; i < Kp; i += kThreads)
+    for (int o = tid; o < Kp / 8; o += kThreads)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) act[(size_t(t) * rows_pad + row) * Kp + i] = 0;
+      for (int t = 0; t < NT; ++t) *lane_ptr(t, o) = make_uint4(0, 0, 0, 0);
     return;
   }
   const size_t base = size_t(row) * H;
@@ -151,35 +159,51 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
     r = float(1.0 / sqrt(tot / double(H_u) + double(eps)));
     if (tid == 0 && r_out) r_out[row] = r;
   }
-  for (int u0 = 0; u0 < Kp; u0 += kBurst) {  // one memory latency per burst
-    float x[kPer], g[kPer];
+  constexpr int kOct = kPer / 8;  // octets per thread per burst
+  for (int o0 = 0; o0 < Kp / 8; o0 += kOct * kThreads) {  // one memory latency per burst
+    float x[kOct][8], g[kOct][8];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int u = u0 + tid + i * kThreads;
-      x[i] = 0.0f;
-      g[i] = 1.0f;
-      if (u < K) {
-        const int h = pad_s ? u + int(fastdiv(uint32_t(u), pdiv)) : u;
-        x[i] = load_hidden<DT>(src, base + h);
-        if constexpr (NORM) g[i] = gamma[h];
-      }
-    }
+    for (int i = 0; i < kOct; ++i)
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int u = u0 + tid + i * kThreads;
-      if (u >= Kp) continue;
-      float y = 0.0f;
-      if (u < K) {
-        if constexpr (NORM) y = deferred ? x[i] * g[i] : (x[i] * r) * g[i];
-        else y = x[i];
+      for (int j = 0; j < 8; ++j) {
+        const int o = o0 + tid + i * kThreads;
+        const int u = 32 * (o / 4) + 4 * (o % 4) + (j & 3) + 16 * (j >> 2);
+        x[i][j] = 0.0f;
+        g[i][j] = 1.0f;
+        if (u < K) {
+          const int h = pad_s ? u + int(fastdiv(uint32_t(u), pdiv)) : u;
+          x[i][j] = load_hidden<DT>(src, base + h);
+          if constexpr (NORM) g[i][j] = gamma[h];
+        }
       }
-      const int slot = k_slot(u);
-      float rem = y;
+#pragma unroll
+    for (int i = 0; i < kOct; ++i) {
+      const int o = o0 + tid + i * kThreads;
+      if (o >= Kp / 8) continue;
+      uint16_t term[NT][8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int u = 32 * (o / 4) + 4 * (o % 4) + (j & 3) + 16 * (j >> 2);
+        float y = 0.0f;
+        if (u < K) {
+          if constexpr (NORM) y = deferred ? x[i][j] * g[i][j] : (x[i][j] * r) * g[i][j];
+          else y = x[i][j];
+        }
+        float rem = y;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          term[t][j] = bf16_rne(rem);
+          rem = rem - bf16_val(term[t][j]);
+        }
+      }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const uint16_t b = bf16_rne(rem);
-        act[(size_t(t) * rows_pad + row) * Kp + slot] = b;
-        rem = rem - bf16_val(b);
+        uint4 v;
+        v.x = uint32_t(term[t][0]) | (uint32_t(term[t][1]) << 16);
+        v.y = uint32_t(term[t][2]) | (uint32_t(term[t][3]) << 16);
+        v.z = uint32_t(term[t][4]) | (uint32_t(term[t][5]) << 16);
+        v.w = uint32_t(term[t][6]) | (uint32_t(term[t][7]) << 16);
+        *lane_ptr(t, o) = v;
       }
     }
   }

@@ -99,7 +99,8 @@ constexpr int kKStep = 64;  // K granularity of the matrix-core path
 int mfma_terms(int gbs);    // bf16 terms per activation for that batch size
 
 // Split (and, with norm, RMS-normalize) activations for the matrix-core path:
-// act [nt][rows_pad][Kp] bf16 bits over the K contraction lanes; r [gbs]
+// act holds nt * rows_pad * Kp bf16 bits over the K contraction lanes as 1 KB
+// MFMA operand fragments ordered (term, 16-row tile, 32-lane K block); r [gbs]
 // (norm only, may be NULL).
 hipError_t launch_split(const void* src, int dtype, bool norm, const float* gamma, int gbs, int H,
                         int H_u, int K, int pad_s, float eps, bool deferred, int nt, int rows_pad,
