@@ -62,9 +62,15 @@ def copy_calibration():
     print(json.dumps(dict(copy_calibration_bytes=n, copies=3)), flush=True)
 
 
+# the sources the gbs-1 RMSNorm + lm_head kernel is built from
+GEMV_SOURCES = ("lm_head_gemv.hip", "tail_internal.h")
+
+
 def kernel_source_hash():
+    """Hash of the dominant kernel's sources; the committed counter summary
+    carries the hash it was measured on."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(os.path.join(ROOT, "decode_sampling_tail_amd", "csrc"))):
+    for name in GEMV_SOURCES:
         with open(os.path.join(ROOT, "decode_sampling_tail_amd", "csrc", name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
