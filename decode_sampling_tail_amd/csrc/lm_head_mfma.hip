@@ -7,8 +7,8 @@
 // The fp32 activations arrive split into NT bf16 terms A_0 + A_1 (+ A_2)
 // (each term the bf16 rounding of what the earlier terms left), so every
 // product in v_mfma_f32_16x16x32_bf16 is exact and accumulates in fp32; two
-// terms represent an activation to 2^-17 relative, three to 2^-26.  The
-// weight itself is bf16 and is never rounded.
+// terms (what the library uses) represent an activation to 2^-17 relative,
+// three to 2^-26.  The weight itself is bf16 and is never rounded.
 //
 // Tiling: a workgroup owns VT consecutive vocabulary columns for BROWS =
 // 16 * NBT batch rows and walks the (unpadded) hidden dimension in K-steps
@@ -451,22 +451,21 @@ hipError_t launch_cfg(const uint16_t* act, int rows_pad, int Kp, const uint16_t*
 
 }  // namespace
 
-int mfma_terms(int gbs) { return gbs <= 64 ? 3 : 2; }
+int mfma_terms(int) { return 2; }
 
 hipError_t launch_lm_head_mfma(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V,
                                int H_u, int pad_s, const float* row_scale, int gbs, float* logits,
                                uint32_t* gkey, hipStream_t st) {
-  const int nt = mfma_terms(gbs);
   for (int b0 = 0; b0 < gbs; b0 += 256) {
     const int rows = gbs - b0 < 256 ? gbs - b0 : 256;
     const int nbt = (rows + 15) / 16;
     hipError_t e;
-    if (nt == 3) {
+    if (nbt <= 4) {
       // 512-column tiles (393 workgroups for GPT-OSS, all resident at once)
-      // and 32-row K-steps: about 32 KB of weight loads in flight per workgroup
-      if (nbt <= 1) e = launch_cfg<512, 4, 1, 1, 3, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else if (nbt <= 2) e = launch_cfg<512, 4, 2, 2, 3, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else e = launch_cfg<512, 4, 2, 4, 3, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      // and 32-row K-steps
+      if (nbt <= 1) e = launch_cfg<512, 4, 1, 1, 2, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      else if (nbt <= 2) e = launch_cfg<512, 4, 2, 2, 2, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      else e = launch_cfg<512, 8, 2, 4, 2, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
     } else {
       // persistent, direct-copy kernel; rows past the chunk are never stored
       if (nbt <= 8) e = launch_dma<256, 2, 4, 8, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);

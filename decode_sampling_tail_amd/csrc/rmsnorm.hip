@@ -244,12 +244,9 @@ hipError_t launch_split(const void* src, int dtype, bool norm, const float* gamm
 #define TAIL_SPLIT(DT, NT, NORM)                                                              \
   hipLaunchKernelGGL((split_kernel<DT, NT, NORM>), grid, block, 0, st, src, gamma, H, H_u, K, \
                      pad_s, pdiv, eps, int(deferred), gbs, rows_pad, Kp, act, r)
+  if (nt != 2) return hipErrorInvalidValue;  // the matrix-core path uses two terms
   if (!norm) {
-    if (nt == 3) TAIL_SPLIT(0, 3, false); else TAIL_SPLIT(0, 2, false);
-  } else if (nt == 3) {
-    if (dtype == 0) TAIL_SPLIT(0, 3, true);
-    else if (dtype == 1) TAIL_SPLIT(1, 3, true);
-    else TAIL_SPLIT(2, 3, true);
+    TAIL_SPLIT(0, 2, false);
   } else {
     if (dtype == 0) TAIL_SPLIT(0, 2, true);
     else if (dtype == 1) TAIL_SPLIT(1, 2, true);

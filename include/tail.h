@@ -100,9 +100,8 @@ int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int
  *                      the sum in fp32 over the real (non-pad) lanes.  The
  *                      activations are never rounded to a single bf16: the
  *                      weight-streaming path (gbs <= 4) uses them as fp32;
- *                      the matrix-core path splits each into bf16 terms
- *                      whose sum keeps it to 2^-26 relative (3 terms, gbs <=
- *                      64) or 2^-17 (2 terms, larger batches).
+ *                      the matrix-core path (gbs > 4) splits each into two
+ *                      bf16 terms whose sum keeps it to 2^-17 relative.
  *   ws, ws_bytes       workspace of at least tail_workspace_size() bytes,
  *                      256-byte aligned (may be NULL when that size is 0).
  * Only TAIL_ZERO_PAD is meaningful in `flags`.
