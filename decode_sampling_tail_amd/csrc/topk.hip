@@ -18,9 +18,10 @@
 //  c. Lists longer than 2k are cut to the k-th largest value v* (radix select)
 //     and, when ties at v* would still leave more than 2k, to the lowest
 //     indices among the elements equal to v* (radix select on ~index).
-//  d. Each survivor's rank is the number of survivors with a larger composite
-//     key (up to 4 threads per survivor); ranks below k are written out (and
-//     kept in LDS for the sampler).
+//  d. Survivors are counting-sorted into 256 bins of their value key; a
+//     survivor's rank is its bin's start plus the number of larger composite
+//     keys in its own bin (about one entry on typical rows); ranks below k
+//     are written out (and kept in LDS for the sampler).
 //  e. More than kCap elements >= t0 (massive ties): the same two cuts are
 //     found by radix passes that re-read the candidate groups, then only the
 //     k winners are collected.  Exact for any input, slow only for such rows.
@@ -40,6 +41,8 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kCap = 4096;                        // LDS candidate capacity
 constexpr int kPerThread = kCap / kSelThreads;    // candidates per thread in registers
 constexpr int kGPer = kMaxGroups / kSelThreads;   // group keys per thread in registers
+// the final ranking keeps 2k composites and 2k value bits in the group list's space
+static_assert(kMaxGroups >= 6 * TAIL_K_MAX, "group list too small for the sorted copy");
 constexpr int kBatch = 4;                         // float4 loads in flight per thread
 
 __device__ inline uint32_t wave_max_u32(uint32_t v) {
@@ -78,6 +81,7 @@ struct SelShared {
   float top_v[TAIL_K_MAX];   // the sorted result, for the sampler
   int32_t top_i[TAIL_K_MAX];
   uint32_t hist[256];
+  uint32_t bstart[257];     // bin starts of the final ranking
   uint32_t bc[4];
   uint32_t cnt, nact;
 };
@@ -424,35 +428,81 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     n = s.cnt;
   }
 
-  // d. rank by composite key; the k best go out in order.  TP threads share a
-  // candidate, each comparing it with every TP-th pair of the list; all lanes
-  // of a wave read the same few pairs at once (LDS broadcast).
-  if (n & 1) {  // pad to an even count with a key below every candidate
-    if (tid == 0) s.c[n] = 0ull;
+  // d. exact ranks by a counting sort on the value keys: the survivors are
+  // binned by (khi - key) >> bsh into 256 bins (bin 0 holds the largest
+  // keys), the bins are laid out in order by an exclusive prefix sum, and a
+  // survivor's rank is its bin's start plus the number of entries of its own
+  // bin with a larger composite key (larger value, then lower index).  A bin
+  // holds about one survivor on typical rows; equal keys share a bin.
+  {
+    uint32_t klo = 0xFFFFFFFFu, khi = 0;
+    for (int i = tid; i < int(n); i += kSelThreads) {
+      const uint32_t v = uint32_t(s.c[i] >> 32);
+      klo = min(klo, v);
+      khi = max(khi, v);
+    }
+    klo = wave_min_u32(klo);
+    khi = wave_max_u32(khi);
+    if (tid < 256) s.hist[tid] = 0;
+    if (tid == 0) {
+      s.bc[0] = 0xFFFFFFFFu;
+      s.bc[1] = 0u;
+    }
     __syncthreads();
-  }
-  const int n2 = int(n + 1) / 2;
-  const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(s.c);
-  const int TP = int(n) * 4 <= kSelThreads ? 4 : (int(n) * 2 <= kSelThreads ? 2 : 1);
-  for (int base = 0; base < int(n) * TP; base += kSelThreads) {
-    const int slot = base + tid;
-    const int i = slot / TP, q = slot % TP;
-    uint64_t ci = i < int(n) ? s.c[i] : ~0ull;
-    uint32_t rank = 0;
-    int j = q;
-    for (; j + 3 * TP < n2; j += 4 * TP) {
-      const ulonglong2 a = c2[j], b = c2[j + TP], c = c2[j + 2 * TP], d = c2[j + 3 * TP];
-      rank += (a.x > ci) + (a.y > ci) + (b.x > ci) + (b.y > ci) + (c.x > ci) + (c.y > ci) +
-              (d.x > ci) + (d.y > ci);
+    if (lane == 0) {
+      atomicMin(&s.bc[0], klo);
+      atomicMax(&s.bc[1], khi);
     }
-    for (; j < n2; j += TP) {
-      const ulonglong2 a = c2[j];
-      rank += (a.x > ci) + (a.y > ci);
+    __syncthreads();
+    klo = s.bc[0];
+    khi = s.bc[1];
+    const uint32_t kspan = khi - klo;
+    const int bsh = kspan < 256u ? 0 : 32 - __clz(int(kspan >> 8));  // (kspan >> bsh) < 256
+    for (int i = tid; i < int(n); i += kSelThreads)
+      atomicAdd(&s.hist[(khi - uint32_t(s.c[i] >> 32)) >> bsh], 1u);
+    __syncthreads();
+    if (tid < 64) {  // exclusive prefix over the bins, 4 per lane; hist becomes the fill cursor
+      uint32_t c[4], loc = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = s.hist[4 * tid + j];
+        loc += c[j];
+      }
+      uint32_t incl = loc;
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = (uint32_t)__shfl_up((int)incl, off, 64);
+        if (tid >= off) incl += t;
+      }
+      uint32_t run = incl - loc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s.bstart[4 * tid + j] = run;
+        s.hist[4 * tid + j] = run;
+        run += c[j];
+      }
+      if (tid == 63) s.bstart[256] = run;
     }
-    for (int off = 1; off < TP; off <<= 1) rank += (uint32_t)__shfl_xor((int)rank, off, 64);
-    if (q == 0 && i < int(n) && rank < uint32_t(k)) {
-      s.top_v[rank] = __uint_as_float(s.cb[i]);
-      s.top_i[rank] = int(~uint32_t(ci));
+    __syncthreads();
+    // the candidate-group list is no longer needed: it holds the sorted copy
+    uint64_t* sc = reinterpret_cast<uint64_t*>(s.act);  // n <= 2k composites
+    uint32_t* sbits = s.act + 2 * (2 * TAIL_K_MAX);     // and their value bits
+    for (int i = tid; i < int(n); i += kSelThreads) {
+      const uint64_t ci = s.c[i];
+      const uint32_t pos = atomicAdd(&s.hist[(khi - uint32_t(ci >> 32)) >> bsh], 1u);
+      sc[pos] = ci;
+      sbits[pos] = s.cb[i];
+    }
+    __syncthreads();
+    for (int i = tid; i < int(n); i += kSelThreads) {
+      const uint64_t ci = sc[i];
+      const int bin = int((khi - uint32_t(ci >> 32)) >> bsh);
+      const int j0 = int(s.bstart[bin]), j1 = int(s.bstart[bin + 1]);
+      uint32_t rank = uint32_t(j0);
+      for (int j = j0; j < j1; ++j) rank += sc[j] > ci;
+      if (rank < uint32_t(k)) {
+        s.top_v[rank] = __uint_as_float(sbits[i]);
+        s.top_i[rank] = int(~uint32_t(ci));
+      }
     }
   }
   __syncthreads();
