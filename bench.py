@@ -10,10 +10,12 @@ bf16 hidden, sampling at top_k 256, top_p 1, T 1, u 0.5, logits not emitted.
 `value` is tokens/s = gbs * K / (time of K steps), timed with HIP events on
 the stream the library launches on, bracketed by device synchronizations.
 
-Also reported: per-stage times, the lm_head kernel's algorithmic HBM rate
-against the 8 TB/s peak (`roofline`), the same numbers at gbs 8 / 64 / 256
-(`by_gbs`), and the fp64 CPU oracle timed on a bounded sample of the
-headline workload (`cpu_baseline`).  Progress goes to stderr; stdout carries
+Also reported: per-step p10/p50/p90, the step with logits emitted, per-stage
+times, the lm_head kernel's algorithmic HBM rate against the 8 TB/s peak
+(`roofline`), the same numbers at gbs 8 / 64 / 256 (`by_gbs`, with the
+matrix-core kernels' executed TFLOP/s against the 2.5 PFLOP/s dense bf16
+peak), and the fp64 CPU oracle timed on a bounded sample of the headline
+workload (`cpu_baseline`).  Progress goes to stderr; stdout carries
 exactly one JSON line.
 """
 import argparse
@@ -29,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "tail tokens/s at gbs 1/8/64/256, V=201088; lm_head HBM GB/s & MFMA % of peak"
 HBM_PEAK = 8000.0  # GB/s, MI355X HBM3E
+MFMA_PEAK = 2500.0  # TFLOP/s, MI355X dense bf16 matrix cores
 COUNTERS = os.path.join(ROOT, "profiles", "rmsnorm_lm_head_gbs1_counters.md")
 
 
@@ -42,7 +45,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="headline workload only")
+    ap.add_argument("--workload", default=None,
+                    help="time only this workload label (for per-workload profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -111,18 +116,30 @@ def gpu_inputs(cid, torch, np):
                      params=torch.from_numpy(np.ascontiguousarray(inp.params[run])).to(dev)), run
 
 
-def time_loop(torch, fn, steps, warmup):
+def time_loop(torch, fn, steps, warmup, per_step=False):
+    """Seconds per call over `steps` calls after `warmup` untimed ones, from
+    HIP events on the stream the library launches on, bracketed by device
+    synchronizations.  With per_step, an event also separates every call and
+    (mean, [p10, p50, p90]) is returned."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(st)
-    for _ in range(steps):
+    n_ev = steps + 1 if per_step else 2
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev[0].record(st)
+    for i in range(steps):
         fn()
-    e1.record(st)
+        if per_step:
+            ev[i + 1].record(st)
+    ev[-1].record(st)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / 1000.0 / steps  # seconds per call
+    mean = ev[0].elapsed_time(ev[-1]) / 1000.0 / steps
+    if not per_step:
+        return mean
+    import numpy as np
+    d = np.array([ev[i].elapsed_time(ev[i + 1]) / 1000.0 for i in range(steps)])
+    return mean, [float(np.percentile(d, q)) for q in (10, 50, 90)]
 
 
 def bench_workload(cid, args, torch, np):
@@ -130,8 +147,14 @@ def bench_workload(cid, args, torch, np):
     inp, g, run = gpu_inputs(cid, torch, np)
     f = dst.Forward(inp.gbs, inp.H, inp.V, inp.k, inp.H_u, inp.eps, inp.zero_pad, deferred=True,
                     emit_logits=False)
-    t_step = time_loop(torch, lambda: f(g["hidden"], g["gamma"], g["w_t"], g["params"]),
-                       args.steps, args.warmup)
+    t_step, pct = time_loop(torch, lambda: f(g["hidden"], g["gamma"], g["w_t"], g["params"]),
+                            args.steps, args.warmup, per_step=True)
+    # the same step with the fp32 logits emitted (an extra gbs*V*4-byte write)
+    fe = dst.Forward(inp.gbs, inp.H, inp.V, inp.k, inp.H_u, inp.eps, inp.zero_pad, deferred=True,
+                     emit_logits=True)
+    t_emit = time_loop(torch, lambda: fe(g["hidden"], g["gamma"], g["w_t"], g["params"]),
+                       max(10, args.steps // 4), args.warmup)
+    del fe
     # stage by stage.  rmsnorm_lm_head runs the same kernels and launch shapes
     # as tail_forward's first stage (there they also emit the group maxima);
     # topk and sample are the standalone calls (inside tail_forward the group
@@ -156,10 +179,16 @@ def bench_workload(cid, args, torch, np):
                 inp.gbs * inp.V * 4 + inp.gbs * 4)
     flops = 2.0 * inp.gbs * inp.H_u * inp.V
     res = dict(gbs=inp.gbs, tokens_per_s=inp.gbs / t_step, steps_per_s=1.0 / t_step,
-               ms_per_step=t_step * 1e3,
+               ms_per_step=t_step * 1e3, ms_p10_p50_p90=[x * 1e3 for x in pct],
+               ms_per_step_emit_logits=t_emit * 1e3,
                stage_us=dict(rmsnorm_lm_head=t_lm * 1e6, topk=t_topk * 1e6, sample=t_samp * 1e6),
                lm_head_gbs=lm_bytes / t_lm / 1e9, lm_head_tflops=flops / t_lm / 1e12,
                lm_head_bytes=lm_bytes)
+    if inp.gbs > 4:
+        # matrix-core path: 2 bf16 activation terms over rows padded to 16
+        exec_flops = 2.0 * ((inp.gbs + 15) // 16 * 16) * 2 * inp.H_u * inp.V
+        res["lm_head_mfma_exec_tflops"] = exec_flops / t_lm / 1e12
+        res["lm_head_mfma_frac"] = exec_flops / t_lm / 1e12 / MFMA_PEAK
     del g, f, logits, ws, r
     torch.cuda.empty_cache()
     return inp, run, res
@@ -206,6 +235,8 @@ def main():
     for label, cid in workloads():
         if args.no_sweep and cid != 1:
             continue
+        if args.workload and label != args.workload:
+            continue
         log(f"workload {label}: generating inputs and timing {args.steps} steps")
         inp, run, res = bench_workload(cid, args, torch, np)
         log(f"{label}: {res['tokens_per_s']:.1f} tok/s, {res['ms_per_step']:.3f} ms/step, "
@@ -214,6 +245,9 @@ def main():
         if cid == 1:
             head_inp, head_run = inp, run
 
+    if "gptoss_tail_gbs1" not in results:  # a profiling run of another workload
+        print(json.dumps(dict(metric=METRIC, by_gbs=results)), flush=True)
+        return
     head = results["gptoss_tail_gbs1"]
     traffic = counter_traffic()
     roof = dict(bound="hbm", achieved=head["lm_head_gbs"], peak=HBM_PEAK, unit="GB/s",
@@ -230,9 +264,8 @@ def main():
                            sampling="top_k=256 top_p=1 T=1 u=0.5", emit_logits=False,
                            parallelism="none (one GPU, whole vocabulary)"),
                stage_us=head["stage_us"], roofline=roof,
-               by_gbs={lbl: dict(gbs=r["gbs"], tokens_per_s=r["tokens_per_s"], ms_per_step=r["ms_per_step"],
-                                 lm_head_gbs=r["lm_head_gbs"], lm_head_hbm_frac=r["lm_head_gbs"] / HBM_PEAK,
-                                 lm_head_tflops=r["lm_head_tflops"], stage_us=r["stage_us"])
+               ms_p10_p50_p90=head["ms_p10_p50_p90"],
+               by_gbs={lbl: dict(r, lm_head_hbm_frac=r["lm_head_gbs"] / HBM_PEAK)
                        for lbl, r in results.items()},
                source_hash=kernel_source_hash())
     if not args.no_cpu_baseline:
