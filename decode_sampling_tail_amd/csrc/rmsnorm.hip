@@ -143,25 +143,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
     return;
   }
   const size_t base = size_t(row) * H;
-  float r = 1.0f;
-  if constexpr (NORM) {
-    float x[kPer];
-    double ss = 0.0;
-    for (int h0 = 0; h0 < H; h0 += kBurst) {
-      load_burst<DT>(src, base, h0, H, pad_s, tid, x);
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) ss = fma(double(x[i]), double(x[i]), ss);
-    }
-    ss = wave_sum(ss);
-    if ((tid & 63) == 0) s_part[tid >> 6] = ss;
-    __syncthreads();
-    const double tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
-    r = float(1.0 / sqrt(tot / double(H_u) + double(eps)));
-    if (tid == 0 && r_out) r_out[row] = r;
-  }
   constexpr int kOct = kPer / 8;  // octets per thread per burst
-  for (int o0 = 0; o0 < Kp / 8; o0 += kOct * kThreads) {  // one memory latency per burst
-    float x[kOct][8], g[kOct][8];
+  // loads the lanes of octets o0 + tid + i * kThreads (zero past K)
+  auto load_octets = [&](int o0, float (&x)[kOct][8], float (&g)[kOct][8]) {
 #pragma unroll
     for (int i = 0; i < kOct; ++i)
 #pragma unroll
@@ -176,6 +160,9 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
           if constexpr (NORM) g[i][j] = gamma[h];
         }
       }
+  };
+  // splits and stores the loaded octets
+  auto emit_octets = [&](int o0, const float (&x)[kOct][8], const float (&g)[kOct][8], float r) {
 #pragma unroll
     for (int i = 0; i < kOct; ++i) {
       const int o = o0 + tid + i * kThreads;
@@ -206,6 +193,49 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
         *lane_ptr(t, o) = v;
       }
     }
+  };
+  auto finish_r = [&](double ss) {  // fixed-order block sum of the per-thread partials
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) s_part[tid >> 6] = ss;
+    __syncthreads();
+    const double tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+    const float r = float(1.0 / sqrt(tot / double(H_u) + double(eps)));
+    if (tid == 0 && r_out) r_out[row] = r;
+    return r;
+  };
+
+  if (Kp / 8 <= kOct * kThreads) {
+    // the whole row in one burst, kept in registers: one memory latency
+    float x[kOct][8], g[kOct][8];
+    load_octets(0, x, g);
+    float r = 1.0f;
+    if constexpr (NORM) {
+      double ss = 0.0;
+#pragma unroll
+      for (int i = 0; i < kOct; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fma(double(x[i][j]), double(x[i][j]), ss);
+      r = finish_r(ss);
+    }
+    emit_octets(0, x, g, r);
+    return;
+  }
+  // longer rows: the sum of squares first, then the split, burst by burst
+  float r = 1.0f;
+  if constexpr (NORM) {
+    float x[kPer];
+    double ss = 0.0;
+    for (int h0 = 0; h0 < H; h0 += kBurst) {
+      load_burst<DT>(src, base, h0, H, pad_s, tid, x);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) ss = fma(double(x[i]), double(x[i]), ss);
+    }
+    r = finish_r(ss);
+  }
+  for (int o0 = 0; o0 < Kp / 8; o0 += kOct * kThreads) {
+    float x[kOct][8], g[kOct][8];
+    load_octets(o0, x, g);
+    emit_octets(o0, x, g, r);
   }
 }
 
