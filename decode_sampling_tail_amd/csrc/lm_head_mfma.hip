@@ -66,8 +66,8 @@ __device__ inline bf16x8 tr_operand(const unsigned char* s_w, int row, int col_b
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int VT, int WV, int WB, int NBT, int NT, int KT = 64>
-__global__ __launch_bounds__(WV * WB * 64) void mfma_kernel(
+template <int VT, int WV, int WB, int NBT, int NT, int KT = 64, int MINB = 1>
+__global__ __launch_bounds__(WV * WB * 64, MINB) void mfma_kernel(
     const uint16_t* __restrict__ act, int rows_pad, int Kp, const uint16_t* __restrict__ w, int V,
     int H_u, int pad_s, FastDiv pdiv, const float* __restrict__ row_scale, int gbs, int b0,
     float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups) {
@@ -437,14 +437,14 @@ hipError_t launch_dma(const uint16_t* act, int rows_pad, int Kp, const uint16_t*
   return hipGetLastError();
 }
 
-template <int VT, int WV, int WB, int NBT, int NT, int KT = 64>
+template <int VT, int WV, int WB, int NBT, int NT, int KT = 64, int MINB = 1>
 hipError_t launch_cfg(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V, int H_u,
                       int pad_s, const float* row_scale, int gbs, int b0, float* logits,
                       uint32_t* gkey, hipStream_t st) {
   const FastDiv pdiv = make_fastdiv(pad_s > 1 ? uint32_t(pad_s - 1) : 1u);
   const int groups = (V + kFusedGroup - 1) / kFusedGroup;
   dim3 grid((V + VT - 1) / VT), block(WV * WB * 64);
-  hipLaunchKernelGGL((mfma_kernel<VT, WV, WB, NBT, NT, KT>), grid, block, 0, st, act, rows_pad, Kp, w, V,
+  hipLaunchKernelGGL((mfma_kernel<VT, WV, WB, NBT, NT, KT, MINB>), grid, block, 0, st, act, rows_pad, Kp, w, V,
                      H_u, pad_s, pdiv, row_scale, gbs, b0, logits, gkey, groups);
   return hipGetLastError();
 }
@@ -460,16 +460,16 @@ hipError_t launch_lm_head_mfma(const uint16_t* act, int rows_pad, int Kp, const 
     const int rows = gbs - b0 < 256 ? gbs - b0 : 256;
     const int nbt = (rows + 15) / 16;
     hipError_t e;
-    if (nbt <= 4) {
-      // 512-column tiles (393 workgroups for GPT-OSS, all resident at once)
-      // and 32-row K-steps
+    if (nbt <= 8) {
+      // 512-column tiles (393 workgroups for GPT-OSS) and 32-row K-steps;
+      // up to 64 rows two workgroups share a CU, so all are resident at once
       if (nbt <= 1) e = launch_cfg<512, 4, 1, 1, 2, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else if (nbt <= 2) e = launch_cfg<512, 4, 2, 2, 2, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else e = launch_cfg<512, 8, 2, 4, 2, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      else if (nbt <= 2) e = launch_cfg<512, 4, 1, 2, 2, 32, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      else if (nbt <= 4) e = launch_cfg<512, 4, 1, 4, 2, 32, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      else e = launch_cfg<512, 4, 2, 8, 2, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
     } else {
       // persistent, direct-copy kernel; rows past the chunk are never stored
-      if (nbt <= 8) e = launch_dma<256, 2, 4, 8, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else e = launch_dma<256, 2, 4, 16, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      e = launch_dma<256, 2, 4, 16, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
     }
     if (e != hipSuccess) return e;
   }
