@@ -35,6 +35,12 @@ silent (each also listed in the design notes):
 * the GEMM input is NOT rounded to bf16 (full-precision activations);
 * top-k runs on the logits themselves; ties go to the lower index and
   -0.0 equals +0.0; inputs must be finite;
+* page precision (optional, ``page=True`` in ``tail``): the page's own
+  numerics, from ``deferred_rms`` (one bf16 rounding of the GEMM input per
+  element), ``skip_nan_fold`` (bf16 products summed at full width) and
+  ``emit_logits`` (the top-k sees the bf16 mirror of the fp32 logits).  The
+  rounded activation is computed in float32, as the device computes it, so
+  both sides take the same rounding decisions;
 * sampler: top-k cut first, then a softmax at T over the kept kk
   candidates, then the nucleus (smallest prefix whose mass is >= top_p of
   the kept mass), then the inverse CDF at u in candidate order (candidate i
@@ -174,21 +180,78 @@ def sample(vals: np.ndarray, idx: np.ndarray, params: np.ndarray) -> tuple[np.nd
     return np.array(toks, dtype=np.int64), diags
 
 
+# ------------------------------------------------------- 7. page precision
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """float32 values -> the nearest bfloat16 value, ties to the even one,
+    returned as float64.  A bf16 keeps the top 16 bits of a float32, so this
+    rounds the low 16 bits away: add 0x7FFF plus the lowest kept bit and
+    truncate.  NaN stays NaN."""
+    f = np.ascontiguousarray(a, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    out = (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(np.isnan(f), np.nan, out)
+
+
+def rmsnorm_page(x: np.ndarray, gamma: np.ndarray, H_u: int, eps: float, pad: np.ndarray,
+                 deferred: bool = True) -> tuple[np.ndarray, np.ndarray]:
+    """The GEMM input at the page's precision (``deferred_rms``: one bf16
+    rounding per element; ``gamma``, ``eps``, ``hidden_actual``).
+
+    r = fp32(1 / sqrt(ms + eps)) with ms the float64 mean square over the
+    real lanes.  Deferred: a = bf16(fp32(x * gamma)) and the row is scaled
+    by r after the contraction.  In-chain: a = bf16(fp32(fp32(x * r) *
+    gamma)) and the scale is 1.  Products are float32 (IEEE, nearest even),
+    as the device forms them.  Returns (a [gbs, H] float64, exact bf16
+    values, 0 on pad lanes; scale [gbs] float64)."""
+    x = np.array(x, dtype=np.float64)
+    g = np.asarray(gamma, dtype=np.float32).reshape(-1)
+    real = ~pad
+    xr = x[:, real]
+    ms = np.sum(xr * xr, axis=1) / float(H_u)
+    r32 = (1.0 / np.sqrt(ms + float(eps))).astype(np.float32)
+    x32 = xr.astype(np.float32)
+    if deferred:
+        y32 = x32 * g[real][None, :]
+        scale = r32.astype(np.float64)
+    else:
+        y32 = (x32 * r32[:, None]) * g[real][None, :]
+        scale = np.ones(x.shape[0])
+    a = np.zeros_like(x)
+    a[:, real] = bf16_round(y32)
+    return a, scale
+
+
+def mirror(L: np.ndarray) -> np.ndarray:
+    """The bf16 mirror of the fp32 logits (``emit_logits``: what the page's
+    top-k ranks): bf16(fp32(L)), as float64."""
+    return bf16_round(np.asarray(L, dtype=np.float64).astype(np.float32))
+
+
 # ------------------------------------------------------------------ the tail
 def tail(hidden, dtype, gamma, w_bits, H_u, k, eps=1e-5, zero_pad=True, params=None,
-         rows=None):
+         rows=None, page=False, deferred=True):
     """The whole tail for every row (or only `rows`, which the oracle may do
     because rows are independent).  Returns a dict with y, r, logits, vals,
-    idx and, when params is given, tokens and diag."""
+    idx and, when params is given, tokens and diag.  With page=True the
+    GEMM input is the page-precision activation (``deferred`` picks its
+    realization), y holds it, and the top-k ranks the bf16 mirror (vals are
+    mirror values)."""
     H = hidden.shape[1]
     pad = pad_mask(H, H_u, zero_pad)
     x = widen(hidden, dtype)
     if rows is not None:
         x = x[rows]
         params = None if params is None else np.asarray(params)[rows]
-    y, r = rmsnorm(x, gamma, H_u, eps, pad)
-    L = logits(y, w_bits, pad)
-    vals, idx = topk(L, k)
+    if page:
+        y, scale = rmsnorm_page(x, gamma, H_u, eps, pad, deferred)
+        r = rmsnorm(x, gamma, H_u, eps, pad)[1]
+        L = logits(y, w_bits, pad) * scale[:, None]
+        vals, idx = topk(mirror(L), k)
+    else:
+        y, r = rmsnorm(x, gamma, H_u, eps, pad)
+        L = logits(y, w_bits, pad)
+        vals, idx = topk(L, k)
     out = dict(y=y, r=r, logits=L, vals=vals, idx=idx)
     if params is not None:
         out["tokens"], out["diag"] = sample(vals, idx, params)
