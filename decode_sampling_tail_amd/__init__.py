@@ -7,8 +7,9 @@ synchronize.  There is no CPU fallback: if the library is not built, loading
 it raises.
 
 The names mirror the C entry points in include/tail.h:
-rmsnorm, lm_head, rmsnorm_lm_head, topk, sample, forward, workspace_size,
-status_string.
+rmsnorm, lm_head, rmsnorm_lm_head, topk, topk_mirror, sample, forward,
+workspace_size, status_string.  ``page=True`` selects TAIL_PAGE_PRECISION
+(bf16 GEMM input, top-k over the bf16 logit mirror).
 """
 from __future__ import annotations
 
@@ -20,11 +21,11 @@ LIB_PATH = os.path.join(_HERE, "libtail.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 F32, F16, BF16 = 0, 1, 2
-EMIT_LOGITS, ZERO_PAD, DEFERRED_RMS = 1, 2, 4
+EMIT_LOGITS, ZERO_PAD, DEFERRED_RMS, PAGE_PRECISION = 1, 2, 4, 8
 K_MAX, GBS_MAX, H_MAX = 1024, 4096, 65536
 
-EXPORTS = ("tail_rmsnorm", "tail_lm_head", "tail_rmsnorm_lm_head", "tail_topk", "tail_sample",
-           "tail_forward", "tail_workspace_size", "tail_status_string")
+EXPORTS = ("tail_rmsnorm", "tail_lm_head", "tail_rmsnorm_lm_head", "tail_topk", "tail_topk_mirror",
+           "tail_sample", "tail_forward", "tail_workspace_size", "tail_status_string")
 
 _lib = None
 
@@ -47,6 +48,7 @@ def lib() -> ctypes.CDLL:
         L.tail_lm_head.argtypes = [vp, vp, vp, i, i, i, i, u, vp, vp, sz, vp]
         L.tail_rmsnorm_lm_head.argtypes = [vp, i, vp, vp, i, i, i, i, f, u, vp, vp, vp, sz, vp]
         L.tail_topk.argtypes = [vp, i, i, i, vp, vp, vp, sz, vp]
+        L.tail_topk_mirror.argtypes = [vp, i, i, i, vp, vp, vp, sz, vp]
         L.tail_sample.argtypes = [vp, vp, i, i, vp, i, vp, vp]
         L.tail_forward.argtypes = [vp, i, vp, vp, i, i, i, i, i, f, u, vp, i, vp, vp, vp, vp, vp, sz, vp]
         L.tail_workspace_size.argtypes = [i, i, i, i, i, u]
@@ -54,7 +56,7 @@ def lib() -> ctypes.CDLL:
         L.tail_status_string.argtypes = [i]
         L.tail_status_string.restype = ctypes.c_char_p
         for name in ("tail_rmsnorm", "tail_lm_head", "tail_rmsnorm_lm_head", "tail_topk",
-                     "tail_sample", "tail_forward"):
+                     "tail_topk_mirror", "tail_sample", "tail_forward"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -114,11 +116,13 @@ def _call(name, *args):
         raise TailError(name, st)
 
 
-def _flags(zero_pad=False, deferred=False, emit=False) -> int:
-    return (ZERO_PAD if zero_pad else 0) | (DEFERRED_RMS if deferred else 0) | (EMIT_LOGITS if emit else 0)
+def _flags(zero_pad=False, deferred=False, emit=False, page=False) -> int:
+    return ((ZERO_PAD if zero_pad else 0) | (DEFERRED_RMS if deferred else 0) |
+            (EMIT_LOGITS if emit else 0) | (PAGE_PRECISION if page else 0))
 
 
-def rmsnorm(hidden, gamma, H_u=None, eps=1e-5, zero_pad=False, deferred=False, out_y=None, out_r=None):
+def rmsnorm(hidden, gamma, H_u=None, eps=1e-5, zero_pad=False, deferred=False, out_y=None, out_r=None,
+            page=False):
     """tail_rmsnorm: returns (y [gbs,H] fp32, r [gbs] fp32)."""
     torch = _torch()
     dev = _dev(hidden)
@@ -127,11 +131,11 @@ def rmsnorm(hidden, gamma, H_u=None, eps=1e-5, zero_pad=False, deferred=False, o
     y = out_y if out_y is not None else torch.empty((gbs, H), dtype=torch.float32, device=dev)
     r = out_r if out_r is not None else torch.empty((gbs,), dtype=torch.float32, device=dev)
     _call("tail_rmsnorm", _ptr(hidden), _hidden_dtype(hidden), _ptr(gamma), gbs, H, H_u, eps,
-          _flags(zero_pad, deferred), _ptr(y), _ptr(r), _stream(dev))
+          _flags(zero_pad, deferred, page=page), _ptr(y), _ptr(r), _stream(dev))
     return y, r
 
 
-def lm_head(y, w_t, H_u=None, zero_pad=False, row_scale=None, out=None, ws=None):
+def lm_head(y, w_t, H_u=None, zero_pad=False, row_scale=None, out=None, ws=None, page=False):
     """tail_lm_head: logits [gbs,V] fp32 = row_scale * (y @ W)."""
     torch = _torch()
     dev = _dev(y)
@@ -140,22 +144,22 @@ def lm_head(y, w_t, H_u=None, zero_pad=False, row_scale=None, out=None, ws=None)
     H_u = H if H_u is None else H_u
     logits = out if out is not None else torch.empty((gbs, V), dtype=torch.float32, device=dev)
     if ws is None:
-        n = workspace_size(gbs, H, H_u, V, 1, _flags(zero_pad, emit=True))
+        n = workspace_size(gbs, H, H_u, V, 1, _flags(zero_pad, emit=True, page=page))
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     _call("tail_lm_head", _ptr(y), _ptr(_weight(w_t)), _ptr(row_scale), gbs, H, H_u, V,
-          _flags(zero_pad), _ptr(logits), _ptr(ws), ws.numel(), _stream(dev))
+          _flags(zero_pad, page=page), _ptr(logits), _ptr(ws), ws.numel(), _stream(dev))
     return logits
 
 
 def rmsnorm_lm_head(hidden, gamma, w_t, H_u=None, eps=1e-5, zero_pad=False, deferred=True, out=None,
-                    out_r=None, ws=None):
+                    out_r=None, ws=None, page=False):
     """tail_rmsnorm_lm_head: (logits [gbs,V] fp32, r [gbs] fp32)."""
     torch = _torch()
     dev = _dev(hidden)
     gbs, H = hidden.shape
     V = w_t.shape[1]
     H_u = H if H_u is None else H_u
-    flags = _flags(zero_pad, deferred)
+    flags = _flags(zero_pad, deferred, page=page)
     logits = out if out is not None else torch.empty((gbs, V), dtype=torch.float32, device=dev)
     r = out_r if out_r is not None else torch.empty((gbs,), dtype=torch.float32, device=dev)
     if ws is None:
@@ -166,8 +170,9 @@ def rmsnorm_lm_head(hidden, gamma, w_t, H_u=None, eps=1e-5, zero_pad=False, defe
     return logits, r
 
 
-def topk(logits, k, out_vals=None, out_idx=None, ws=None):
-    """tail_topk: (vals [gbs,k] fp32 descending, idx [gbs,k] int32)."""
+def topk(logits, k, out_vals=None, out_idx=None, ws=None, mirror=False):
+    """tail_topk (or tail_topk_mirror: ranks the bf16 rounding of the
+    logits): (vals [gbs,k] fp32 descending, idx [gbs,k] int32)."""
     torch = _torch()
     dev = _dev(logits)
     gbs, V = logits.shape
@@ -175,7 +180,8 @@ def topk(logits, k, out_vals=None, out_idx=None, ws=None):
     idx = out_idx if out_idx is not None else torch.empty((gbs, k), dtype=torch.int32, device=dev)
     if ws is None:
         ws = torch.empty(max(workspace_size(gbs, 1, 1, V, k, EMIT_LOGITS), 1), dtype=torch.uint8, device=dev)
-    _call("tail_topk", _ptr(logits), gbs, V, k, _ptr(vals), _ptr(idx), _ptr(ws), ws.numel(), _stream(dev))
+    _call("tail_topk_mirror" if mirror else "tail_topk", _ptr(logits), gbs, V, k, _ptr(vals), _ptr(idx),
+          _ptr(ws), ws.numel(), _stream(dev))
     return vals, idx
 
 
@@ -195,12 +201,12 @@ class Forward:
     fixed shapes (what a decode loop or a benchmark wants)."""
 
     def __init__(self, gbs, H, V, k=256, H_u=None, eps=1e-5, zero_pad=False, deferred=True,
-                 emit_logits=True, device="cuda"):
+                 emit_logits=True, device="cuda", page=False):
         torch = _torch()
         self.gbs, self.H, self.V, self.k = gbs, H, V, k
         self.H_u = H if H_u is None else H_u
         self.eps = eps
-        self.flags = _flags(zero_pad, deferred, emit_logits)
+        self.flags = _flags(zero_pad, deferred, emit_logits, page)
         self.device = torch.device(device)
         dev = self.device
         self.logits = torch.empty((gbs, V), dtype=torch.float32, device=dev) if emit_logits else None
@@ -224,8 +230,9 @@ class Forward:
 
 
 def forward(hidden, gamma, w_t, k=256, H_u=None, eps=1e-5, zero_pad=False, deferred=True,
-            emit_logits=True, params=None):
+            emit_logits=True, params=None, page=False):
     """tail_forward with freshly allocated outputs; returns a dict of tensors."""
     gbs, H = hidden.shape
-    f = Forward(gbs, H, w_t.shape[1], k, H_u, eps, zero_pad, deferred, emit_logits, hidden.device)
+    f = Forward(gbs, H, w_t.shape[1], k, H_u, eps, zero_pad, deferred, emit_logits, hidden.device,
+                page)
     return f(hidden, gamma, w_t, params)

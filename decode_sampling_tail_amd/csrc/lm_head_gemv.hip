@@ -28,6 +28,11 @@
 // own K range with y = x * gamma, so no barrier delays the weight stream, and
 // r (scale) is finished in the epilogue.  In-chain: the whole row's r comes
 // first and y = (x * r) * gamma (scale = 1).
+//
+// Page precision (parameters "deferred_rms" and "skip_nan_fold": one bf16
+// rounding of the GEMM input per element, bf16 products summed in fp32):
+// every activation is rounded to bf16 where it is formed (fused) or read
+// (given y); the products with the bf16 weights are then exact in fp32.
 #include "tail_internal.h"
 
 #include <hip/hip_fp16.h>
@@ -68,6 +73,7 @@ struct GemvArgs {
   float eps;               // fused only
   int H_u;                 // fused only: mean-square divisor
   int deferred;            // fused only
+  int page;                // round the activations to bf16
   const uint16_t* w;
   const float* row_scale;  // SRC < 0 only (may be NULL)
   int K, pad_s, V;
@@ -146,7 +152,10 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
           for (int i = 0; i < kBurst; ++i) {
             const int u = c0 + lane + 64 * i;
             ss = fma(double(x[i]), double(x[i]), ss);
-            if (u < u1) s_y[b * K + u] = x[i] * g[i];
+            if (u < u1) {
+              const float yv = x[i] * g[i];
+              s_y[b * K + u] = a.page ? bf16_round(yv) : yv;
+            }
           }
         }
         ss = wave_sum(ss);
@@ -180,7 +189,8 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
         scale[b] = 1.0f;
         for (int u = tid; u < K; u += kThreads) {
           const int hp = pad_s ? u + int(fastdiv(uint32_t(u), a.pdiv)) : u;
-          s_y[b * K + u] = (s_y[b * K + u] * r) * a.gamma[hp];
+          const float yv = (s_y[b * K + u] * r) * a.gamma[hp];
+          s_y[b * K + u] = a.page ? bf16_round(yv) : yv;
         }
         if (tid == 0 && a.r_out) a.r_out[a.b0 + b] = r;
       }
@@ -198,6 +208,7 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
     for (int c = 0; c < 8; ++c) acc[b][c] = 0.0f;
 
   const float* yg = static_cast<const float*>(a.src) + size_t(a.b0) * a.ldsrc;
+  const bool page_src = SRC < 0 && a.page;
   for (int u = u0; u < u1; u += U) {
     uint4 nx[U];
     int nh[U];
@@ -212,7 +223,8 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
         yv[b][j] = 0.0f;
         if (u + j < u1) {
           if constexpr (SRC >= 0) yv[b][j] = s_y[b * K + u + j];
-          else yv[b][j] = yg[size_t(b) * a.ldsrc + hh[j]];
+          else yv[b][j] = page_src ? bf16_round(yg[size_t(b) * a.ldsrc + hh[j]])
+                                   : yg[size_t(b) * a.ldsrc + hh[j]];
         }
       }
 #pragma unroll
@@ -336,9 +348,10 @@ bool gemv_fusable(int gbs, int K) {
 }
 
 hipError_t launch_lm_head_gemv(const float* y, int ldy, const uint16_t* w, const float* row_scale,
-                               int gbs, int K, int pad_s, int V, float* logits, uint32_t* gkey,
-                               hipStream_t st) {
+                               int gbs, int K, int pad_s, int V, bool page, float* logits,
+                               uint32_t* gkey, hipStream_t st) {
   GemvArgs a{};
+  a.page = page ? 1 : 0;
   a.src = y;
   a.ldsrc = ldy;
   a.w = w;
@@ -361,9 +374,11 @@ hipError_t launch_lm_head_gemv(const float* y, int ldy, const uint16_t* w, const
 }
 
 hipError_t launch_norm_gemv(const void* hidden, int dtype, const float* gamma, int gbs, int H,
-                            int H_u, int K, int pad_s, float eps, bool deferred, const uint16_t* w,
-                            int V, float* logits, float* r_out, uint32_t* gkey, hipStream_t st) {
+                            int H_u, int K, int pad_s, float eps, bool deferred, bool page,
+                            const uint16_t* w, int V, float* logits, float* r_out, uint32_t* gkey,
+                            hipStream_t st) {
   GemvArgs a{};
+  a.page = page ? 1 : 0;
   a.src = hidden;
   a.ldsrc = H;
   a.gamma = gamma;

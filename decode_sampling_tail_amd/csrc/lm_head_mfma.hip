@@ -7,8 +7,10 @@
 // The fp32 activations arrive split into NT bf16 terms A_0 + A_1 (+ A_2)
 // (each term the bf16 rounding of what the earlier terms left), so every
 // product in v_mfma_f32_16x16x32_bf16 is exact and accumulates in fp32; two
-// terms (what the library uses) represent an activation to 2^-17 relative,
-// three to 2^-26.  The weight itself is bf16 and is never rounded.
+// terms (the default) represent an activation to 2^-17 relative, three to
+// 2^-26.  The page-precision mode uses one term: the activation rounded to
+// bf16 once, as the page's parameter "deferred_rms" describes.  The weight
+// itself is bf16 and is never rounded.
 //
 // Tiling: a workgroup owns VT consecutive vocabulary columns for BROWS =
 // 16 * NBT batch rows and walks the (unpadded) hidden dimension in K-steps
@@ -449,13 +451,10 @@ hipError_t launch_cfg(const uint16_t* act, int rows_pad, int Kp, const uint16_t*
   return hipGetLastError();
 }
 
-}  // namespace
-
-int mfma_terms(int) { return 2; }
-
-hipError_t launch_lm_head_mfma(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V,
-                               int H_u, int pad_s, const float* row_scale, int gbs, float* logits,
-                               uint32_t* gkey, hipStream_t st) {
+template <int NT>
+hipError_t launch_terms(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V,
+                        int H_u, int pad_s, const float* row_scale, int gbs, float* logits,
+                        uint32_t* gkey, hipStream_t st) {
   for (int b0 = 0; b0 < gbs; b0 += 256) {
     const int rows = gbs - b0 < 256 ? gbs - b0 : 256;
     const int nbt = (rows + 15) / 16;
@@ -463,17 +462,31 @@ hipError_t launch_lm_head_mfma(const uint16_t* act, int rows_pad, int Kp, const 
     if (nbt <= 8) {
       // 512-column tiles (393 workgroups for GPT-OSS) and 32-row K-steps;
       // up to 64 rows two workgroups share a CU, so all are resident at once
-      if (nbt <= 1) e = launch_cfg<512, 4, 1, 1, 2, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else if (nbt <= 2) e = launch_cfg<512, 4, 1, 2, 2, 32, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else if (nbt <= 4) e = launch_cfg<512, 4, 1, 4, 2, 32, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else e = launch_cfg<512, 4, 2, 8, 2, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      if (nbt <= 1) e = launch_cfg<512, 4, 1, 1, NT, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      else if (nbt <= 2) e = launch_cfg<512, 4, 1, 2, NT, 32, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      else if (nbt <= 4) e = launch_cfg<512, 4, 1, 4, NT, 32, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      else e = launch_cfg<512, 4, 2, 8, NT, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
     } else {
       // persistent, direct-copy kernel; rows past the chunk are never stored
-      e = launch_dma<256, 2, 4, 16, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      e = launch_dma<256, 2, 4, 16, NT>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
     }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+int mfma_terms(int, bool page) { return page ? 1 : 2; }
+
+hipError_t launch_lm_head_mfma(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,
+                               int V, int H_u, int pad_s, const float* row_scale, int gbs,
+                               float* logits, uint32_t* gkey, hipStream_t st) {
+  if (nt == 2)
+    return launch_terms<2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, logits, gkey, st);
+  if (nt == 1)
+    return launch_terms<1>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, logits, gkey, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tail

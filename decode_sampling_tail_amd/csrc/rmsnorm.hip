@@ -55,7 +55,8 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restrict__ hidden,
                                                            const float* __restrict__ gamma, int H,
                                                            int H_u, int pad_s, float eps,
-                                                           int deferred, float* __restrict__ y,
+                                                           int deferred, int page,
+                                                           float* __restrict__ y,
                                                            float* __restrict__ r_out) {
   __shared__ double s_part[kThreads / 64];
   const int row = blockIdx.x;
@@ -85,6 +86,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restric
         if (!is_pad(h, pad_s)) {
           const float g = gamma[h];
           out = deferred ? x[i] * g : (x[i] * r) * g;
+          if (page) out = bf16_round(out);
         }
         y[base + h] = out;
       }
@@ -113,10 +115,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restric
 // ordered (t, rt, kb), so the fragments of one row tile for consecutive K
 // blocks are contiguous.  Each thread produces one 16-byte lane (an "octet")
 // per term.
-__device__ inline uint16_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
+__device__ inline uint16_t bf16_rne(float f) { return uint16_t(bf16_rne_bits(__float_as_uint(f))); }
 __device__ inline float bf16_val(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 template <int DT, int NT, bool NORM>
@@ -242,21 +241,21 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
 }  // namespace
 
 hipError_t launch_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int H,
-                          int H_u, int pad_s, float eps, bool deferred, float* y, float* r,
-                          hipStream_t st) {
+                          int H_u, int pad_s, float eps, bool deferred, bool page, float* y,
+                          float* r, hipStream_t st) {
   dim3 grid(gbs), block(kThreads);
   switch (dtype) {
     case 0:
       hipLaunchKernelGGL(rmsnorm_kernel<0>, grid, block, 0, st, hidden, gamma, H, H_u, pad_s, eps,
-                         int(deferred), y, r);
+                         int(deferred), int(page), y, r);
       break;
     case 1:
       hipLaunchKernelGGL(rmsnorm_kernel<1>, grid, block, 0, st, hidden, gamma, H, H_u, pad_s, eps,
-                         int(deferred), y, r);
+                         int(deferred), int(page), y, r);
       break;
     default:
       hipLaunchKernelGGL(rmsnorm_kernel<2>, grid, block, 0, st, hidden, gamma, H, H_u, pad_s, eps,
-                         int(deferred), y, r);
+                         int(deferred), int(page), y, r);
       break;
   }
   return hipGetLastError();
@@ -274,13 +273,19 @@ hipError_t launch_split(const void* src, int dtype, bool norm, const float* gamm
 #define TAIL_SPLIT(DT, NT, NORM)                                                              \
   hipLaunchKernelGGL((split_kernel<DT, NT, NORM>), grid, block, 0, st, src, gamma, H, H_u, K, \
                      pad_s, pdiv, eps, int(deferred), gbs, rows_pad, Kp, act, r)
-  if (nt != 2) return hipErrorInvalidValue;  // the matrix-core path uses two terms
-  if (!norm) {
-    TAIL_SPLIT(0, 2, false);
-  } else {
-    if (dtype == 0) TAIL_SPLIT(0, 2, true);
+  // two terms (the default precision) or one (the page-precision mode)
+  if (nt == 2) {
+    if (!norm) TAIL_SPLIT(0, 2, false);
+    else if (dtype == 0) TAIL_SPLIT(0, 2, true);
     else if (dtype == 1) TAIL_SPLIT(1, 2, true);
     else TAIL_SPLIT(2, 2, true);
+  } else if (nt == 1) {
+    if (!norm) TAIL_SPLIT(0, 1, false);
+    else if (dtype == 0) TAIL_SPLIT(0, 1, true);
+    else if (dtype == 1) TAIL_SPLIT(1, 1, true);
+    else TAIL_SPLIT(2, 1, true);
+  } else {
+    return hipErrorInvalidValue;
   }
 #undef TAIL_SPLIT
   return hipGetLastError();

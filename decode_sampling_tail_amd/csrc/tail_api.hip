@@ -12,6 +12,9 @@ namespace {
 
 using tail::align256;
 
+constexpr unsigned kAllFlags =
+    TAIL_EMIT_LOGITS | TAIL_ZERO_PAD | TAIL_DEFERRED_RMS | TAIL_PAGE_PRECISION;
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 size_t dtype_bytes(int dtype) { return dtype == TAIL_F32 ? 4 : 2; }
@@ -46,17 +49,18 @@ int check_k(int V, int k) {
   return TAIL_OK;
 }
 
-// Geometry of the matrix-core path's split activations: [nt][rows_pad][Kp] bf16.
+// Geometry of the matrix-core path's split activations: [nt][rows_pad][Kp] bf16
+// (nt = 1 in the page-precision mode).
 struct SplitGeom {
   int K, Kp, rows_pad, nt;
   size_t bytes;
 };
-SplitGeom split_geom(int gbs, int H, int H_u, int pad_s) {
+SplitGeom split_geom(int gbs, int H, int H_u, int pad_s, unsigned flags) {
   SplitGeom g;
   g.K = pad_s ? H_u : H;
   g.Kp = (g.K + tail::kKStep - 1) / tail::kKStep * tail::kKStep;
   g.rows_pad = (gbs + 15) / 16 * 16;
-  g.nt = tail::mfma_terms(gbs);
+  g.nt = tail::mfma_terms(gbs, flags & TAIL_PAGE_PRECISION);
   g.bytes = gbs > tail::kGemvMaxBatch ? size_t(g.nt) * g.rows_pad * g.Kp * 2 : 0;
   return g;
 }
@@ -75,7 +79,7 @@ FwdLayout forward_layout(int gbs, int H, int H_u, int pad_s, int V, int k, unsig
   L.r = off;
   off = align256(off + size_t(gbs) * 4);
   L.act = off;
-  off = align256(off + split_geom(gbs, H, H_u, pad_s).bytes);
+  off = align256(off + split_geom(gbs, H, H_u, pad_s, flags).bytes);
   L.logits = off;
   if (!(flags & TAIL_EMIT_LOGITS)) off = align256(off + size_t(gbs) * V * 4);
   L.gkey = off;
@@ -100,25 +104,26 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 // weight-streaming kernel, or the bf16-split producer then the matrix cores.
 // y (gbs*H floats) and act (split_geom bytes) are workspace.
 hipError_t norm_lm_head(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t,
-                        int gbs, int H, int H_u, int V, float eps, int ps, bool deferred, float* y,
+                        int gbs, int H, int H_u, int V, float eps, int ps, unsigned flags, float* y,
                         float* r, uint16_t* act, float* logits, uint32_t* gkey, hipStream_t st) {
-  const SplitGeom sg = split_geom(gbs, H, H_u, ps);
+  const bool deferred = flags & TAIL_DEFERRED_RMS, page = flags & TAIL_PAGE_PRECISION;
+  const SplitGeom sg = split_geom(gbs, H, H_u, ps, flags);
   if (tail::gemv_fusable(gbs, sg.K))
-    return tail::launch_norm_gemv(hidden, dtype, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, w_t,
-                                  V, logits, r, gkey, st);
+    return tail::launch_norm_gemv(hidden, dtype, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, page,
+                                  w_t, V, logits, r, gkey, st);
   hipError_t e;
   if (gbs <= tail::kGemvMaxBatch) {
-    e = tail::launch_rmsnorm(hidden, dtype, gamma, gbs, H, H_u, ps, eps, deferred, y, r, st);
-    if (e == hipSuccess)
-      e = tail::launch_lm_head_gemv(y, H, w_t, deferred ? r : nullptr, gbs, sg.K, ps, V, logits,
-                                    gkey, st);
+    e = tail::launch_rmsnorm(hidden, dtype, gamma, gbs, H, H_u, ps, eps, deferred, page, y, r, st);
+    if (e == hipSuccess)  // y is already rounded in the page mode
+      e = tail::launch_lm_head_gemv(y, H, w_t, deferred ? r : nullptr, gbs, sg.K, ps, V, false,
+                                    logits, gkey, st);
     return e;
   }
   e = tail::launch_split(hidden, dtype, true, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, sg.nt,
                          sg.rows_pad, sg.Kp, act, r, st);
   if (e == hipSuccess)
-    e = tail::launch_lm_head_mfma(act, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps, deferred ? r : nullptr,
-                                  gbs, logits, gkey, st);
+    e = tail::launch_lm_head_mfma(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
+                                  deferred ? r : nullptr, gbs, logits, gkey, st);
   return e;
 }
 
@@ -143,7 +148,7 @@ TAIL_API size_t tail_workspace_size(int gbs, int H, int H_u, int V, int k, unsig
   const int ps = pad_stride(H, H_u, flags);
   size_t fwd = forward_layout(gbs, H, H_u, ps, V, k, flags).total;
   size_t tk = topk_ws_bytes(gbs, V, k);
-  size_t lm = align256(split_geom(gbs, H, H_u, ps).bytes);
+  size_t lm = align256(split_geom(gbs, H, H_u, ps, flags).bytes);
   size_t m = fwd > tk ? fwd : tk;
   return m > lm ? m : lm;
 }
@@ -154,7 +159,7 @@ TAIL_API int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int
   if (int s = check_shape(gbs, H, H_u)) return s;
   if (dtype != TAIL_F32 && dtype != TAIL_F16 && dtype != TAIL_BF16) return TAIL_ERR_INVALID_ARG;
   if (!(eps >= 0.0f) || !isfinite(eps)) return TAIL_ERR_INVALID_ARG;
-  if (flags & ~(TAIL_EMIT_LOGITS | TAIL_ZERO_PAD | TAIL_DEFERRED_RMS)) return TAIL_ERR_INVALID_ARG;
+  if (flags & ~kAllFlags) return TAIL_ERR_INVALID_ARG;
   int ps = pad_stride(H, H_u, flags);
   if (ps < 0) return TAIL_ERR_INVALID_ARG;
   bool deferred = flags & TAIL_DEFERRED_RMS;
@@ -163,7 +168,8 @@ TAIL_API int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int
       (out_r && !aligned(out_r, 4)))
     return TAIL_ERR_INVALID_ARG;
   return hip_status(tail::launch_rmsnorm(hidden, dtype, gamma, gbs, H, H_u, ps, eps, deferred,
-                                         out_y, out_r, (hipStream_t)stream));
+                                         flags & TAIL_PAGE_PRECISION, out_y, out_r,
+                                         (hipStream_t)stream));
 }
 
 TAIL_API int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_scale, int gbs,
@@ -171,25 +177,25 @@ TAIL_API int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_
                           size_t ws_bytes, void* stream) {
   if (int s = check_shape(gbs, H, H_u)) return s;
   if (int s = check_vocab(V)) return s;
-  if (flags & ~(TAIL_EMIT_LOGITS | TAIL_ZERO_PAD | TAIL_DEFERRED_RMS)) return TAIL_ERR_INVALID_ARG;
+  if (flags & ~kAllFlags) return TAIL_ERR_INVALID_ARG;
   int ps = pad_stride(H, H_u, flags);
   if (ps < 0) return TAIL_ERR_INVALID_ARG;
   if (!y || !w_t || !logits) return TAIL_ERR_INVALID_ARG;
   if (!aligned(y, 4) || !aligned(w_t, 16) || !aligned(logits, 16) ||
       (row_scale && !aligned(row_scale, 4)))
     return TAIL_ERR_INVALID_ARG;
-  const SplitGeom sg = split_geom(gbs, H, H_u, ps);
+  const SplitGeom sg = split_geom(gbs, H, H_u, ps, flags);
   if (int s = check_ws(ws, ws_bytes, sg.bytes)) return s;
   hipStream_t st = (hipStream_t)stream;
   if (gbs <= tail::kGemvMaxBatch)
-    return hip_status(tail::launch_lm_head_gemv(y, H, w_t, row_scale, gbs, sg.K, ps, V, logits,
-                                                nullptr, st));
+    return hip_status(tail::launch_lm_head_gemv(y, H, w_t, row_scale, gbs, sg.K, ps, V,
+                                                flags & TAIL_PAGE_PRECISION, logits, nullptr, st));
   uint16_t* act = (uint16_t*)ws;
   hipError_t e = tail::launch_split(y, TAIL_F32, false, nullptr, gbs, H, H_u, sg.K, ps, 0.0f, false,
                                     sg.nt, sg.rows_pad, sg.Kp, act, nullptr, st);
   if (e == hipSuccess)
-    e = tail::launch_lm_head_mfma(act, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps, row_scale, gbs, logits,
-                                  nullptr, st);
+    e = tail::launch_lm_head_mfma(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps, row_scale, gbs,
+                                  logits, nullptr, st);
   return hip_status(e);
 }
 
@@ -201,7 +207,7 @@ TAIL_API int tail_rmsnorm_lm_head(const void* hidden, int dtype, const float* ga
   if (int s = check_vocab(V)) return s;
   if (dtype != TAIL_F32 && dtype != TAIL_F16 && dtype != TAIL_BF16) return TAIL_ERR_INVALID_ARG;
   if (!(eps >= 0.0f) || !isfinite(eps)) return TAIL_ERR_INVALID_ARG;
-  if (flags & ~(TAIL_EMIT_LOGITS | TAIL_ZERO_PAD | TAIL_DEFERRED_RMS)) return TAIL_ERR_INVALID_ARG;
+  if (flags & ~kAllFlags) return TAIL_ERR_INVALID_ARG;
   const int ps = pad_stride(H, H_u, flags);
   if (ps < 0) return TAIL_ERR_INVALID_ARG;
   if (!hidden || !gamma || !w_t || !logits) return TAIL_ERR_INVALID_ARG;
@@ -213,13 +219,14 @@ TAIL_API int tail_rmsnorm_lm_head(const void* hidden, int dtype, const float* ga
   if (int s = check_ws(ws, ws_bytes, L.gkey)) return s;
   char* base = (char*)ws;
   float* r = out_r ? out_r : (float*)(base + L.r);
-  return hip_status(norm_lm_head(hidden, dtype, gamma, w_t, gbs, H, H_u, V, eps, ps,
-                                 flags & TAIL_DEFERRED_RMS, (float*)(base + L.y), r,
+  return hip_status(norm_lm_head(hidden, dtype, gamma, w_t, gbs, H, H_u, V, eps, ps, flags,
+                                 (float*)(base + L.y), r,
                                  (uint16_t*)(base + L.act), logits, nullptr, (hipStream_t)stream));
 }
 
-TAIL_API int tail_topk(const float* logits, int gbs, int V, int k, float* vals, int32_t* idx,
-                       void* ws, size_t ws_bytes, void* stream) {
+namespace {
+int topk_call(const float* logits, int gbs, int V, int k, bool mirror, float* vals, int32_t* idx,
+              void* ws, size_t ws_bytes, void* stream) {
   if (gbs < 1) return TAIL_ERR_INVALID_ARG;
   if (gbs > TAIL_GBS_MAX) return TAIL_ERR_UNSUPPORTED;
   if (int s = check_vocab(V)) return s;
@@ -229,8 +236,19 @@ TAIL_API int tail_topk(const float* logits, int gbs, int V, int k, float* vals, 
   if (int s = check_ws(ws, ws_bytes, topk_ws_bytes(gbs, V, k))) return s;
   tail::TopkGeom g;
   tail::topk_geometry(V, k, &g);
-  return hip_status(tail::launch_topk(logits, gbs, V, k, g, (uint32_t*)ws, vals, idx,
+  return hip_status(tail::launch_topk(logits, gbs, V, k, g, (uint32_t*)ws, mirror, vals, idx,
                                       (hipStream_t)stream));
+}
+}  // namespace
+
+TAIL_API int tail_topk(const float* logits, int gbs, int V, int k, float* vals, int32_t* idx,
+                       void* ws, size_t ws_bytes, void* stream) {
+  return topk_call(logits, gbs, V, k, false, vals, idx, ws, ws_bytes, stream);
+}
+
+TAIL_API int tail_topk_mirror(const float* logits, int gbs, int V, int k, float* vals,
+                              int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  return topk_call(logits, gbs, V, k, true, vals, idx, ws, ws_bytes, stream);
 }
 
 TAIL_API int tail_sample(const float* vals, const int32_t* idx, int gbs, int k,
@@ -254,7 +272,7 @@ TAIL_API int tail_forward(const void* hidden, int dtype, const float* gamma, con
   if (int s = check_k(V, k)) return s;
   if (dtype != TAIL_F32 && dtype != TAIL_F16 && dtype != TAIL_BF16) return TAIL_ERR_INVALID_ARG;
   if (!(eps >= 0.0f) || !isfinite(eps)) return TAIL_ERR_INVALID_ARG;
-  if (flags & ~(TAIL_EMIT_LOGITS | TAIL_ZERO_PAD | TAIL_DEFERRED_RMS)) return TAIL_ERR_INVALID_ARG;
+  if (flags & ~kAllFlags) return TAIL_ERR_INVALID_ARG;
   int ps = pad_stride(H, H_u, flags);
   if (ps < 0) return TAIL_ERR_INVALID_ARG;
   bool emit = flags & TAIL_EMIT_LOGITS;
@@ -276,18 +294,17 @@ TAIL_API int tail_forward(const void* hidden, int dtype, const float* gamma, con
   uint16_t* act = (uint16_t*)(base + L.act);
   float* lg = emit ? logits : (float*)(base + L.logits);
   uint32_t* gk = (uint32_t*)(base + L.gkey);
-  const bool deferred = flags & TAIL_DEFERRED_RMS;
   tail::TopkGeom g;
   tail::topk_geometry(V, k, &g);
-  const SplitGeom sg = split_geom(gbs, H, H_u, ps);
   // group maxima come from the lm_head epilogue when the top-k groups are its
   // 64-column groups; otherwise from a separate pass over the logits
   const bool fused_groups = g.gs == tail::kFusedGroup;
   uint32_t* gk_fused = fused_groups ? gk : nullptr;
-  hipError_t e = norm_lm_head(hidden, dtype, gamma, w_t, gbs, H, H_u, V, eps, ps, deferred, y, r,
-                              act, lg, gk_fused, st);
+  hipError_t e = norm_lm_head(hidden, dtype, gamma, w_t, gbs, H, H_u, V, eps, ps, flags, y, r, act,
+                              lg, gk_fused, st);
   if (e == hipSuccess && !fused_groups) e = tail::launch_group_max(lg, gbs, V, g, gk, st);
   if (e == hipSuccess)
-    e = tail::launch_select(lg, gbs, V, k, g, gk, vals, idx, params, ncols, tokens, st);
+    e = tail::launch_select(lg, gbs, V, k, g, gk, flags & TAIL_PAGE_PRECISION, vals, idx, params,
+                            ncols, tokens, st);
   return hip_status(e);
 }

@@ -47,6 +47,18 @@ __device__ inline uint4 load_stream(const uint16_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// float32 -> bfloat16, round to nearest, ties to even (the bf16 is the upper
+// 16 bits of the result; adding 0x7FFF plus the lowest kept bit carries
+// exactly when the dropped half is above, or at and odd, the midpoint).  A NaN
+// stays a quiet NaN; values past the largest bf16 become infinities.
+__device__ inline uint32_t bf16_rne_bits(uint32_t u) {
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u | 0x00400000u) >> 16;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ inline float bf16_round(float f) {
+  return __uint_as_float(bf16_rne_bits(__float_as_uint(f)) << 16);
+}
+
 // Order-preserving key of a float: larger float <=> larger unsigned key.
 // -0.0 is canonicalized to +0.0 so the two compare equal.
 __device__ inline uint32_t float_key(float f) {
@@ -76,27 +88,31 @@ inline bool topk_geometry(int V, int k, TopkGeom* g) {
 
 // Launchers (each defined next to its kernels).  They assume validated
 // arguments and return the launch status.
+// page: round every output to bf16 (the GEMM input of the page-precision mode)
 hipError_t launch_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int H, int H_u,
-                          int pad_s, float eps, bool deferred, float* y, float* r, hipStream_t st);
+                          int pad_s, float eps, bool deferred, bool page, float* y, float* r,
+                          hipStream_t st);
 
 // Weight-streaming lm_head over K contraction lanes (pad lanes skipped when
 // pad_s > 0).  gkey (may be NULL): per row, the largest order-preserving key
-// of each group of kFusedGroup columns, [gbs, ceil(V / kFusedGroup)].
+// of each group of kFusedGroup columns, [gbs, ceil(V / kFusedGroup)].  page:
+// the activations are rounded to bf16 before the contraction.
 hipError_t launch_lm_head_gemv(const float* y, int ldy, const uint16_t* w, const float* row_scale,
-                               int gbs, int K, int pad_s, int V, float* logits, uint32_t* gkey,
-                               hipStream_t st);
+                               int gbs, int K, int pad_s, int V, bool page, float* logits,
+                               uint32_t* gkey, hipStream_t st);
 
 // The same with the RMSNorm fused into the prologue (hidden rows in their
 // storage dtype); r_out (may be NULL) receives the per-row rms scale.
 bool gemv_fusable(int gbs, int K);
 hipError_t launch_norm_gemv(const void* hidden, int dtype, const float* gamma, int gbs, int H,
-                            int H_u, int K, int pad_s, float eps, bool deferred, const uint16_t* w,
-                            int V, float* logits, float* r_out, uint32_t* gkey, hipStream_t st);
+                            int H_u, int K, int pad_s, float eps, bool deferred, bool page,
+                            const uint16_t* w, int V, float* logits, float* r_out, uint32_t* gkey,
+                            hipStream_t st);
 
 // Batches above this size run the lm_head on the matrix cores.
 constexpr int kGemvMaxBatch = 4;
 constexpr int kKStep = 64;  // K granularity of the matrix-core path
-int mfma_terms(int gbs);    // bf16 terms per activation for that batch size
+int mfma_terms(int gbs, bool page);  // bf16 terms per activation (1 in the page-precision mode)
 
 // Split (and, with norm, RMS-normalize) activations for the matrix-core path:
 // act holds nt * rows_pad * Kp bf16 bits over the K contraction lanes as 1 KB
@@ -106,20 +122,23 @@ hipError_t launch_split(const void* src, int dtype, bool norm, const float* gamm
                         int H_u, int K, int pad_s, float eps, bool deferred, int nt, int rows_pad,
                         int Kp, uint16_t* act, float* r, hipStream_t st);
 
-hipError_t launch_lm_head_mfma(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V,
-                               int H_u, int pad_s, const float* row_scale, int gbs, float* logits,
-                               uint32_t* gkey, hipStream_t st);
+hipError_t launch_lm_head_mfma(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,
+                               int V, int H_u, int pad_s, const float* row_scale, int gbs,
+                               float* logits, uint32_t* gkey, hipStream_t st);
 
 hipError_t launch_group_max(const float* logits, int gbs, int V, const TopkGeom& geom,
                             uint32_t* gkey, hipStream_t st);
 
-// params NULL: no sampling (ncols and tokens unused)
+// params NULL: no sampling (ncols and tokens unused).  mirror: rank the bf16
+// rounding of every logit and return the rounded values (gkey may hold the
+// unrounded group maxima: rounding is monotone, so the rounded maximum is the
+// maximum of the rounded values).
 hipError_t launch_select(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
-                         const uint32_t* gkey, float* vals, int32_t* idx, const float* params,
-                         int ncols, int32_t* tokens, hipStream_t st);
+                         const uint32_t* gkey, bool mirror, float* vals, int32_t* idx,
+                         const float* params, int ncols, int32_t* tokens, hipStream_t st);
 
 hipError_t launch_topk(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
-                       uint32_t* gkey_ws, float* vals, int32_t* idx, hipStream_t st);
+                       uint32_t* gkey_ws, bool mirror, float* vals, int32_t* idx, hipStream_t st);
 
 hipError_t launch_sample(const float* vals, const int32_t* idx, int gbs, int k,
                          const float* params, int ncols, int32_t* tokens, hipStream_t st);

@@ -29,6 +29,13 @@
 //
 // Values are copied from the logits, so -0.0 keeps its sign while ranking
 // equal to +0.0.
+//
+// Mirror mode (parameter "emit_logits": the page's top-k ranks the bf16
+// mirror of the fp32 logits): every element is rounded to bf16 (nearest,
+// ties to even) as it is read, and the rounded value is what is ranked and
+// returned.  The group maxima may come from the unrounded logits: rounding
+// is monotone, so the rounded maximum of a group is the maximum of its
+// rounded elements, and step a's bound holds unchanged.
 #include "sampler_row.h"
 #include "../../include/tail.h"
 
@@ -206,10 +213,24 @@ __device__ inline void wave_append(SelShared& s, bool pred, uint32_t key, int e,
   }
 }
 
+// The bits an element is ranked and returned by: its own, or (mirror) its
+// bf16 rounding.
+template <bool MIRROR>
+__device__ inline uint32_t rank_bits(float x) {
+  if constexpr (MIRROR) return bf16_rne_bits(__float_as_uint(x)) << 16;
+  else return __float_as_uint(x);
+}
+
+// Order-preserving key -> the key of the value's bf16 rounding.
+__device__ inline uint32_t mirror_key(uint32_t key) {
+  const uint32_t bits = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return float_key(__uint_as_float(bf16_rne_bits(bits) << 16));
+}
+
 // Visit every element of the candidate groups, kBatch float4 loads in flight
-// per thread.  f(in, key, e) is called by all lanes of a wave the same number
-// of times (out-of-range slots have in == false).
-template <typename F>
+// per thread.  f(in, key, e, bits) is called by all lanes of a wave the same
+// number of times (out-of-range slots have in == false).
+template <bool MIRROR, typename F>
 __device__ inline void for_candidates(const SelShared& s, const float* row, int V, int gs, int nact,
                                       int tid, F&& f) {
   const int wave_first = tid & ~63;
@@ -235,10 +256,12 @@ __device__ inline void for_candidates(const SelShared& s, const float* row, int 
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        f(in[u], float_key(v[u].x), e[u], __float_as_uint(v[u].x));
-        f(in[u], float_key(v[u].y), e[u] + 1, __float_as_uint(v[u].y));
-        f(in[u], float_key(v[u].z), e[u] + 2, __float_as_uint(v[u].z));
-        f(in[u], float_key(v[u].w), e[u] + 3, __float_as_uint(v[u].w));
+        const uint32_t bx = rank_bits<MIRROR>(v[u].x), by = rank_bits<MIRROR>(v[u].y);
+        const uint32_t bz = rank_bits<MIRROR>(v[u].z), bw = rank_bits<MIRROR>(v[u].w);
+        f(in[u], float_key(__uint_as_float(bx)), e[u], bx);
+        f(in[u], float_key(__uint_as_float(by)), e[u] + 1, by);
+        f(in[u], float_key(__uint_as_float(bz)), e[u] + 2, bz);
+        f(in[u], float_key(__uint_as_float(bw)), e[u] + 3, bw);
       }
     }
   } else {
@@ -251,13 +274,13 @@ __device__ inline void for_candidates(const SelShared& s, const float* row, int 
         e = int(s.act[fi / gs]) * gs + fi % gs;
         in = e < V;
       }
-      const float x = in ? row[e] : 0.0f;
-      f(in, float_key(x), e, __float_as_uint(x));
+      const uint32_t bx = rank_bits<MIRROR>(in ? row[e] : 0.0f);
+      f(in, float_key(__uint_as_float(bx)), e, bx);
     }
   }
 }
 
-template <int P>
+template <int P, bool MIRROR>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ logits, int V, int gs, int groups, int k,
     const uint32_t* __restrict__ gkey, float* __restrict__ vals, int32_t* __restrict__ idx,
@@ -282,6 +305,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int g = tid + j * kSelThreads;
     gk[j] = g < groups ? gkey[size_t(row_id) * groups + g] : 0u;
     if (g < groups) {
+      if constexpr (MIRROR) gk[j] = mirror_key(gk[j]);
       lo = min(lo, gk[j]);
       hi = max(hi, gk[j]);
     }
@@ -346,7 +370,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int nact = int(s.nact);
 
   // b. every element >= t0
-  for_candidates(s, row, V, gs, nact, tid,
+  for_candidates<MIRROR>(s, row, V, gs, nact, tid,
                  [&](bool in, uint32_t key, int e, uint32_t bits) {
                    wave_append(s, in && key >= t0, key, e, bits, lane);
                  });
@@ -356,7 +380,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // e. too many: find the cut by radix passes over the candidate groups
   if (n > uint32_t(kCap)) {
     auto visit_all = [&](auto&& f) {
-      for_candidates(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int, uint32_t) {
+      for_candidates<MIRROR>(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int, uint32_t) {
         if (in && key >= t0) f(key);
       });
     };
@@ -365,7 +389,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (above + equal > uint32_t(kCap)) {
       uint32_t a2, e2;
       const uint32_t nk = radix_kth(s, tid, uint32_t(k) - above, [&](auto&& f) {
-        for_candidates(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int e, uint32_t) {
+        for_candidates<MIRROR>(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int e, uint32_t) {
           if (in && key == vstar) f(~uint32_t(e));
         });
       }, &a2, &e2);
@@ -374,7 +398,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __syncthreads();
     if (tid == 0) s.cnt = 0;
     __syncthreads();
-    for_candidates(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int e, uint32_t bits) {
+    for_candidates<MIRROR>(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int e, uint32_t bits) {
       wave_append(s, in && (key > vstar || (key == vstar && e <= ecut)), key, e, bits, lane);
     });
     __syncthreads();
@@ -532,27 +556,40 @@ hipError_t launch_group_max(const float* logits, int gbs, int V, const TopkGeom&
   return hipGetLastError();
 }
 
-hipError_t launch_select(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
-                         const uint32_t* gkey, float* vals, int32_t* idx, const float* params,
-                         int ncols, int32_t* tokens, hipStream_t st) {
+namespace {
+template <bool MIRROR>
+void select_dispatch(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
+                     const uint32_t* gkey, float* vals, int32_t* idx, const float* params,
+                     int ncols, int32_t* tokens, hipStream_t st) {
   dim3 grid(gbs), block(kSelThreads);
-#define TAIL_SELECT_LAUNCH(P)                                                                     \
-  hipLaunchKernelGGL(select_kernel<P>, grid, block, 0, st, logits, V, geom.gs, geom.groups, k, gkey, \
-                     vals, idx, params, ncols, tokens)
+#define TAIL_SELECT_LAUNCH(P)                                                                  \
+  hipLaunchKernelGGL((select_kernel<P, MIRROR>), grid, block, 0, st, logits, V, geom.gs,       \
+                     geom.groups, k, gkey, vals, idx, params, ncols, tokens)
   if (k <= 64) TAIL_SELECT_LAUNCH(1);
   else if (k <= 128) TAIL_SELECT_LAUNCH(2);
   else if (k <= 256) TAIL_SELECT_LAUNCH(4);
   else if (k <= 512) TAIL_SELECT_LAUNCH(8);
   else TAIL_SELECT_LAUNCH(16);
 #undef TAIL_SELECT_LAUNCH
+}
+}  // namespace
+
+hipError_t launch_select(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
+                         const uint32_t* gkey, bool mirror, float* vals, int32_t* idx,
+                         const float* params, int ncols, int32_t* tokens, hipStream_t st) {
+  if (mirror)
+    select_dispatch<true>(logits, gbs, V, k, geom, gkey, vals, idx, params, ncols, tokens, st);
+  else
+    select_dispatch<false>(logits, gbs, V, k, geom, gkey, vals, idx, params, ncols, tokens, st);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
-                       uint32_t* gkey_ws, float* vals, int32_t* idx, hipStream_t st) {
+                       uint32_t* gkey_ws, bool mirror, float* vals, int32_t* idx, hipStream_t st) {
   hipError_t e = launch_group_max(logits, gbs, V, geom, gkey_ws, st);
   if (e != hipSuccess) return e;
-  return launch_select(logits, gbs, V, k, geom, gkey_ws, vals, idx, nullptr, 0, nullptr, st);
+  return launch_select(logits, gbs, V, k, geom, gkey_ws, mirror, vals, idx, nullptr, 0, nullptr,
+                       st);
 }
 
 }  // namespace tail

@@ -51,6 +51,7 @@ extern "C" {
 #define TAIL_EMIT_LOGITS 1u  /* "emit_logits": write the fp32 [gbs,V] logits */
 #define TAIL_ZERO_PAD 2u     /* "zero_interleaved_pad": skip the interleaved pad lanes */
 #define TAIL_DEFERRED_RMS 4u /* "deferred_rms": apply the row's rms scale after the contraction */
+#define TAIL_PAGE_PRECISION 8u /* the page's own numerics (below) */
 
 /* limits of this build */
 #define TAIL_K_MAX 1024      /* largest k ("k": 256 in production) */
@@ -68,6 +69,17 @@ extern "C" {
  */
 
 /*
+ * Precision ("deferred_rms", "skip_nan_fold", "emit_logits").  By default the
+ * GEMM input keeps (at least) fp32 precision and the top-k ranks the fp32
+ * logits.  TAIL_PAGE_PRECISION selects the page's own numerics instead: the
+ * fp32 activation (x * gamma deferred, (x * r) * gamma in-chain) is rounded
+ * to bf16 once per element (round to nearest, ties to even), the bf16 x bf16
+ * products are summed in fp32, and the top-k ranks the bf16 mirror of the
+ * fp32 logits (each logit rounded to bf16 the same way), returning the mirror
+ * values.  The emitted logits stay fp32.
+ */
+
+/*
  * tail_rmsnorm -- final RMSNorm ("gamma", "eps", "hidden_actual",
  * "hidden_states", "deferred_rms").
  *
@@ -78,10 +90,13 @@ extern "C" {
  *   gamma  [H]       fp32.
  *   eps              >= 0, added to the mean square inside the square root.
  *   out_y  [gbs, H]  fp32: x * r * gamma ("(x*rms)*gamma" order), or x * gamma
- *                    with TAIL_DEFERRED_RMS; pad lanes are written as 0.
+ *                    with TAIL_DEFERRED_RMS; pad lanes are written as 0.  With
+ *                    TAIL_PAGE_PRECISION each value is rounded to bf16 (the
+ *                    GEMM input of that mode), stored as fp32.
  *   out_r  [gbs]     fp32: r = 1/sqrt(mean_{H_u}(x^2) + eps); may be NULL
  *                    unless TAIL_DEFERRED_RMS is set.
- * Only TAIL_ZERO_PAD and TAIL_DEFERRED_RMS are meaningful in `flags`.
+ * TAIL_ZERO_PAD, TAIL_DEFERRED_RMS and TAIL_PAGE_PRECISION are meaningful in
+ * `flags`.
  */
 int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int H, int H_u,
                  float eps, unsigned flags, float* out_y, float* out_r, void* stream);
@@ -97,14 +112,16 @@ int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int
  *                      deferred rms scale), or NULL for none.
  *   logits    [gbs, V] fp32, 16-byte aligned:
  *                      logits[b,v] = row_scale[b] * sum_h y[b,h] * W[h,v],
- *                      the sum in fp32 over the real (non-pad) lanes.  The
- *                      activations are never rounded to a single bf16: the
- *                      weight-streaming path (gbs <= 4) uses them as fp32;
- *                      the matrix-core path (gbs > 4) splits each into two
- *                      bf16 terms whose sum keeps it to 2^-17 relative.
+ *                      the sum in fp32 over the real (non-pad) lanes.  By
+ *                      default the activations are never rounded to a single
+ *                      bf16: the weight-streaming path (gbs <= 4) uses them
+ *                      as fp32; the matrix-core path (gbs > 4) splits each
+ *                      into two bf16 terms whose sum keeps it to 2^-17
+ *                      relative.  With TAIL_PAGE_PRECISION each y[b,h] is
+ *                      first rounded to bf16.
  *   ws, ws_bytes       workspace of at least tail_workspace_size() bytes,
  *                      256-byte aligned (may be NULL when that size is 0).
- * Only TAIL_ZERO_PAD is meaningful in `flags`.
+ * TAIL_ZERO_PAD and TAIL_PAGE_PRECISION are meaningful in `flags`.
  */
 int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_scale, int gbs, int H,
                  int H_u, int V, unsigned flags, float* logits, void* ws, size_t ws_bytes,
@@ -124,7 +141,8 @@ int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_scale, in
  *   logits [gbs, V] fp32, 16-byte aligned.
  *   out_r  [gbs] fp32 or NULL: the per-row rms scale r.
  *   ws, ws_bytes: workspace of at least tail_workspace_size() bytes.
- * TAIL_ZERO_PAD and TAIL_DEFERRED_RMS are meaningful in `flags`.
+ * TAIL_ZERO_PAD, TAIL_DEFERRED_RMS and TAIL_PAGE_PRECISION are meaningful in
+ * `flags`.
  */
 int tail_rmsnorm_lm_head(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t,
                          int gbs, int H, int H_u, int V, float eps, unsigned flags, float* logits,
@@ -143,6 +161,17 @@ int tail_rmsnorm_lm_head(const void* hidden, int dtype, const float* gamma, cons
  */
 int tail_topk(const float* logits, int gbs, int V, int k, float* vals, int32_t* idx, void* ws,
               size_t ws_bytes, void* stream);
+
+/*
+ * tail_topk_mirror -- the same over the bf16 mirror of the logits ("emit_logits":
+ * the page's top-k ranks the bf16 copy of the fp32 logits): every logit is
+ * rounded to bf16 (nearest, ties to even) before ranking, and vals receives
+ * the rounded values (fp32 with zero low 16 bits).  Distinct logits that round
+ * to the same bf16 tie, and ties keep the lower indices.  Arguments and
+ * workspace as for tail_topk.
+ */
+int tail_topk_mirror(const float* logits, int gbs, int V, int k, float* vals, int32_t* idx,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /*
  * tail_sample -- per-row sampler over the k candidates ("sampling_params").
@@ -167,7 +196,8 @@ int tail_sample(const float* vals, const int32_t* idx, int gbs, int k, const flo
  * sampler, all enqueued on `stream`.
  *
  *   hidden, dtype, gamma, w_t, gbs, H, H_u, V, k, eps: as above.
- *   flags:  TAIL_EMIT_LOGITS (write `logits`), TAIL_ZERO_PAD, TAIL_DEFERRED_RMS.
+ *   flags:  TAIL_EMIT_LOGITS (write `logits`), TAIL_ZERO_PAD, TAIL_DEFERRED_RMS,
+ *           TAIL_PAGE_PRECISION (bf16 GEMM input and the top-k of tail_topk_mirror).
  *   params: [gbs, ncols] or NULL; NULL skips the sampler and leaves `tokens`
  *           untouched (tokens may then be NULL).
  *   logits: [gbs, V] fp32, required only with TAIL_EMIT_LOGITS.

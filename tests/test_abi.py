@@ -45,6 +45,7 @@ def test_header_constants_match_binding():
     assert int(consts["TAIL_ZERO_PAD"]) == dst.ZERO_PAD
     assert int(consts["TAIL_DEFERRED_RMS"]) == dst.DEFERRED_RMS
     assert int(consts["TAIL_EMIT_LOGITS"]) == dst.EMIT_LOGITS
+    assert int(consts["TAIL_PAGE_PRECISION"]) == dst.PAGE_PRECISION
     assert int(consts["TAIL_K_MAX"]) == dst.K_MAX
 
 
@@ -137,28 +138,29 @@ def test_rmsnorm_lm_head_validation():
     assert rlh(gbs=64, ws_bytes=1024) == dst.ERR_WORKSPACE   # matrix-core activations need room
 
 
-def tk(**kw):
+def tk(mirror=False, **kw):
     a = dict(logits=P, gbs=2, V=4096, k=16, vals=P, idx=P, ws=P, ws_bytes=1 << 20)
     a.update(kw)
-    return dst.lib().tail_topk(a["logits"], a["gbs"], a["V"], a["k"], a["vals"], a["idx"], a["ws"],
-                               a["ws_bytes"], None)
+    fn = dst.lib().tail_topk_mirror if mirror else dst.lib().tail_topk
+    return fn(a["logits"], a["gbs"], a["V"], a["k"], a["vals"], a["idx"], a["ws"], a["ws_bytes"], None)
 
 
-def test_topk_validation():
+@pytest.mark.parametrize("mirror", [False, True])
+def test_topk_validation(mirror):
     E = dst.ERR_INVALID_ARG
-    assert tk(k=0) == E
-    assert tk(k=4097) == E                                      # k > V
-    assert tk(V=8192, k=dst.K_MAX + 1) == dst.ERR_UNSUPPORTED
-    assert tk(gbs=0) == E
-    assert tk(logits=NULL) == E
-    assert tk(vals=NULL) == E
-    assert tk(idx=NULL) == E
-    assert tk(V=4100) == dst.ERR_UNSUPPORTED
-    assert tk(ws=NULL) == dst.ERR_WORKSPACE
-    assert tk(ws=ctypes.c_void_p(0x100010)) == dst.ERR_WORKSPACE
+    assert tk(mirror, k=0) == E
+    assert tk(mirror, k=4097) == E                                      # k > V
+    assert tk(mirror, V=8192, k=dst.K_MAX + 1) == dst.ERR_UNSUPPORTED
+    assert tk(mirror, gbs=0) == E
+    assert tk(mirror, logits=NULL) == E
+    assert tk(mirror, vals=NULL) == E
+    assert tk(mirror, idx=NULL) == E
+    assert tk(mirror, V=4100) == dst.ERR_UNSUPPORTED
+    assert tk(mirror, ws=NULL) == dst.ERR_WORKSPACE
+    assert tk(mirror, ws=ctypes.c_void_p(0x100010)) == dst.ERR_WORKSPACE
     # 16 groups of 256 columns per row: 2 rows * 16 * 4 bytes of group maxima, in
     # one 256-byte aligned block
-    assert tk(ws_bytes=255) == dst.ERR_WORKSPACE
+    assert tk(mirror, ws_bytes=255) == dst.ERR_WORKSPACE
     assert dst.workspace_size(2, 1, 1, 4096, 16, dst.EMIT_LOGITS) >= 256
 
 
@@ -201,7 +203,7 @@ def test_forward_validation():
     assert fwd(w=NULL) == E
     assert fwd(dtype=7) == E
     assert fwd(k=257, V=256) == E
-    assert fwd(H=3072, H_u=2880, flags=dst.ZERO_PAD | 8) == E   # unknown flag bit
+    assert fwd(H=3072, H_u=2880, flags=dst.ZERO_PAD | 16) == E  # unknown flag bit
     assert fwd(ws=NULL) == dst.ERR_WORKSPACE
     need = dst.workspace_size(8, 2880, 2880, 201088, 256, dst.EMIT_LOGITS)
     assert fwd(ws_bytes=need - 1) == dst.ERR_WORKSPACE
@@ -222,3 +224,8 @@ def test_workspace_size():
         cur = ws(gbs, 2880, 2880, 201088, 256, 0)
         assert cur > prev
         prev = cur
+    # the page-precision mode keeps one bf16 term of the activations, not two
+    full = ws(64, 2880, 2880, 201088, 256, dst.EMIT_LOGITS)
+    page = ws(64, 2880, 2880, 201088, 256, dst.EMIT_LOGITS | dst.PAGE_PRECISION)
+    assert full - page == 64 * 2880 * 2
+    assert ws(1, 2880, 2880, 201088, 256, 0) == ws(1, 2880, 2880, 201088, 256, dst.PAGE_PRECISION)
