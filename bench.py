@@ -11,7 +11,7 @@ bf16 hidden, sampling at top_k 256, top_p 1, T 1, u 0.5, logits not emitted.
 the stream the library launches on, bracketed by device synchronizations.
 
 Also reported: per-step p10/p50/p90, the step with logits emitted, per-stage
-times, the lm_head kernel's algorithmic HBM rate against the 8 TB/s peak
+times, the page-precision mode's step and lm_head (`page_precision`), the lm_head kernel's algorithmic HBM rate against the 8 TB/s peak
 (`roofline`), the same numbers at gbs 8 / 64 / 256 (`by_gbs`, with the
 matrix-core kernels' executed TFLOP/s against the 2.5 PFLOP/s dense bf16
 peak), and the fp64 CPU oracle timed on a bounded sample of the headline
@@ -195,7 +195,27 @@ def bench_workload(cid, args, torch, np):
         exec_flops = 2.0 * ((inp.gbs + 15) // 16 * 16) * 2 * inp.H_u * inp.V
         res["lm_head_mfma_exec_tflops"] = exec_flops / t_lm / 1e12
         res["lm_head_mfma_frac"] = exec_flops / t_lm / 1e12 / MFMA_PEAK
-    del g, f, logits, ws, r
+    # the page-precision mode (bf16 GEMM input, top-k over the bf16 mirror):
+    # the same step and stage, one activation term on the matrix cores
+    fp = dst.Forward(inp.gbs, inp.H, inp.V, inp.k, inp.H_u, inp.eps, inp.zero_pad, deferred=True,
+                     emit_logits=False, page=True)
+    t_page = time_loop(torch, lambda: fp(g["hidden"], g["gamma"], g["w_t"], g["params"]),
+                       args.steps, args.warmup)
+    del fp
+    wsp = torch.empty(dst.workspace_size(inp.gbs, inp.H, inp.H_u, inp.V, inp.k,
+                                         dst.EMIT_LOGITS | dst.PAGE_PRECISION),
+                      dtype=torch.uint8, device="cuda")
+    t_lm_page = time_loop(torch, lambda: dst.rmsnorm_lm_head(
+        g["hidden"], g["gamma"], g["w_t"], inp.H_u, inp.eps, inp.zero_pad, True, out=logits, out_r=r,
+        ws=wsp, page=True), args.steps, args.warmup)
+    page = dict(tokens_per_s=inp.gbs / t_page, ms_per_step=t_page * 1e3,
+                rmsnorm_lm_head_us=t_lm_page * 1e6, lm_head_gbs=lm_bytes / t_lm_page / 1e9)
+    if inp.gbs > 4:
+        exec_flops = 2.0 * ((inp.gbs + 15) // 16 * 16) * inp.H_u * inp.V
+        page["lm_head_mfma_exec_tflops"] = exec_flops / t_lm_page / 1e12
+        page["lm_head_mfma_frac"] = exec_flops / t_lm_page / 1e12 / MFMA_PEAK
+    res["page_precision"] = page
+    del g, f, logits, ws, wsp, r
     torch.cuda.empty_cache()
     return inp, run, res
 
@@ -246,7 +266,9 @@ def main():
         log(f"workload {label}: generating inputs and timing {args.steps} steps")
         inp, run, res = bench_workload(cid, args, torch, np)
         log(f"{label}: {res['tokens_per_s']:.1f} tok/s, {res['ms_per_step']:.3f} ms/step, "
-            f"lm_head {res['lm_head_gbs']:.0f} GB/s, stages {res['stage_us']}")
+            f"lm_head {res['lm_head_gbs']:.0f} GB/s, stages {res['stage_us']}; page precision "
+            f"{res['page_precision']['tokens_per_s']:.1f} tok/s, lm_head "
+            f"{res['page_precision']['rmsnorm_lm_head_us']:.1f} us")
         results[label] = res
         if cid == 1:
             head_inp, head_run = inp, run

@@ -206,16 +206,16 @@ __global__ __launch_bounds__(WV * WB * 64, MINB) void mfma_kernel(
 }
 
 // Persistent form for batches above 64 rows, with direct global-to-LDS copies
-// (global_load_lds_dwordx4) and a three-stage LDS ring.
+// (global_load_lds_dwordx4) and an NS-stage LDS ring.
 //
 // The grid holds as many workgroups as fit on the device at once; workgroup
 // w owns the contiguous range of 64-column key groups [w G / P, (w + 1) G / P)
 // (G groups, P workgroups), so every workgroup gets the same number of
 // columns to within one group, and walks it in sub-tiles of VT columns (the
 // last one may be narrower), one K-step of 32 rows at a time.  The K-steps of
-// all its sub-tiles form one pipeline: the copies for step q + 2 go out while
-// step q runs, without passing through registers, so two steps of memory
-// latency are hidden; one barrier per step.  Wave (wv, wb) owns tiles
+// all its sub-tiles form one pipeline: the copies for step q + NS - 1 go out
+// while step q runs, without passing through registers, so NS - 1 steps of
+// memory latency are hidden; one barrier per step.  Wave (wv, wb) owns tiles
 // wv * VTW .. wv * VTW + VTW - 1 (16 columns each) of the sub-tile for rows
 // (wb * BTW .. wb * BTW + BTW - 1) * 16 of the 16 * NBT-row chunk.  A
 // sub-tile's logits and its 64-column group maxima are written from the
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(WV * WB * 64, MINB) void mfma_kernel(
 // Rows past K and columns past V are fetched from clamped (valid) addresses:
 // a clamped weight row meets zero activations, and clamped columns or row
 // tiles only reach outputs that are never stored.
-template <int VT, int WV, int WB, int NBT, int NT>
+template <int VT, int WV, int WB, int NBT, int NT, int NS>
 struct DCfg {
   static constexpr int NW = WV * WB, NTH = NW * 64;
   static constexpr int VTW = VT / 16 / WV, BTW = NBT / WB;
@@ -241,8 +241,8 @@ struct DCfg {
   static constexpr int WAIT = NINS / NW;                           // fewest copies of any wave
   static constexpr int STAGE = WBYTES + BINS * 1024;
   static_assert(VTW * 16 * WV == VT && VTW % 4 == 0 && BTW * WB == NBT && WPITCH <= 1024 &&
-                    VT >= 128 && (VT & (VT - 1)) == 0 && WAIT >= 1 && WAIT < 64 &&
-                    3 * STAGE <= 160 * 1024,
+                    VT >= 128 && (VT & (VT - 1)) == 0 && WAIT >= 1 && NS >= 2 &&
+                    WAIT * (NS - 2) < 64 && NS * STAGE <= 160 * 1024,
                 "tile");
 };
 
@@ -254,13 +254,25 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int VT, int WV, int WB, int NBT, int NT>
+// Wait until at most W * n of this wave's memory operations are outstanding
+// (n <= N, wave-uniform).
+template <int W, int N>
+__device__ inline void wait_steps(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N) wait_vmcnt<W * N>();
+    else wait_steps<W, N - 1>(n);
+  }
+}
+
+template <int VT, int WV, int WB, int NBT, int NT, int NS>
 __global__ __launch_bounds__(WV * WB * 64) void dma_kernel(
     const uint16_t* __restrict__ act, int rows_pad, int Kp, const uint16_t* __restrict__ w, int V,
     int K, int pad_s, FastDiv pdiv, const float* __restrict__ row_scale, int gbs, int b0,
     float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups) {
-  using C = DCfg<VT, WV, WB, NBT, NT>;
-  __shared__ __align__(1024) unsigned char smem[3 * C::STAGE];
+  using C = DCfg<VT, WV, WB, NBT, NT, NS>;
+  __shared__ __align__(1024) unsigned char smem[NS * C::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -276,11 +288,11 @@ __global__ __launch_bounds__(WV * WB * 64) void dma_kernel(
   if (total <= 0) return;
   const int rtiles = rows_pad / 16;
 
-  // this wave's copies of step q into stage (q % 3)
+  // this wave's copies of step q into stage (q % NS)
   auto issue = [&](int q) {
     const int j = q / nks, ks = q % nks;
     const int v0 = c0 + j * VT;
-    unsigned char* st = smem + (q % 3) * C::STAGE;
+    unsigned char* st = smem + (q % NS) * C::STAGE;
     for (int i = wave; i < C::NINS; i += C::NW) {
       if (i < C::WINS) {
         const int r = i * C::RPI + lane / (64 / C::RPI);
@@ -332,23 +344,22 @@ __global__ __launch_bounds__(WV * WB * 64) void dma_kernel(
     tr_addr[vt] = smem_base + tr_row * C::WPITCH + ch * 16 + 8 * (s16 & 3);
   }
 
-  issue(0);
-  if (total > 1) issue(1);
+  for (int p = 0; p < NS - 1 && p < total; ++p) issue(p);
   for (int q = 0; q < total; ++q) {
-    // this wave's copies of step q are done once at most those of step q + 1
-    // are outstanding; the barrier extends that to every wave, and also
-    // retires every wave's reads of step q - 1, whose stage step q + 2 reuses
-    if (q + 1 < total) wait_vmcnt<C::WAIT>();
-    else wait_vmcnt<0>();
+    // this wave's copies of step q are done once at most those of the steps
+    // after it that are already issued are outstanding (copies complete in
+    // issue order); the barrier extends that to every wave, and also retires
+    // every wave's reads of step q - 1, whose stage step q + NS - 1 reuses
+    wait_steps<C::WAIT, NS - 2>(min(NS - 2, total - 1 - q));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (q + 2 < total) issue(q + 2);
+    if (q + NS - 1 < total) issue(q + NS - 1);
 
     const int j = q / nks, ks = q % nks;
     const int v0 = c0 + j * VT, vend = min(v0 + VT, c1);
     const int ntile = __builtin_amdgcn_readfirstlane((vend - v0 + 15) / 16 - wv * C::VTW);
-    const uint32_t soff = uint32_t((q % 3) * C::STAGE);
-    const unsigned char* st = smem + (q % 3) * C::STAGE;
+    const uint32_t soff = uint32_t((q % NS) * C::STAGE);
+    const unsigned char* st = smem + (q % NS) * C::STAGE;
     s16x4 alo[C::VTW], ahi[C::VTW];
 #pragma unroll
     for (int vt = 0; vt < C::VTW; ++vt) {
@@ -413,11 +424,11 @@ __global__ __launch_bounds__(WV * WB * 64) void dma_kernel(
   }
 }
 
-template <int VT, int WV, int WB, int NBT, int NT>
+template <int VT, int WV, int WB, int NBT, int NT, int NS>
 hipError_t launch_dma(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V, int K,
                       int pad_s, const float* row_scale, int gbs, int b0, float* logits,
                       uint32_t* gkey, hipStream_t st) {
-  auto kern = dma_kernel<VT, WV, WB, NBT, NT>;
+  auto kern = dma_kernel<VT, WV, WB, NBT, NT, NS>;
   static int per_cu = -1;
   if (per_cu < 0) {
     int n = 0;
@@ -467,8 +478,9 @@ hipError_t launch_terms(const uint16_t* act, int rows_pad, int Kp, const uint16_
       else if (nbt <= 4) e = launch_cfg<512, 4, 1, 4, NT, 32, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
       else e = launch_cfg<512, 4, 2, 8, NT, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
     } else {
-      // persistent, direct-copy kernel; rows past the chunk are never stored
-      e = launch_dma<256, 2, 4, 16, NT>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      // persistent, direct-copy kernel; rows past the chunk are never stored.
+      // One term leaves LDS for a fourth ring stage.
+      e = launch_dma<256, 2, 4, 16, NT, NT == 1 ? 4 : 3>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
     }
     if (e != hipSuccess) return e;
   }
