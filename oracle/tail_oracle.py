@@ -34,7 +34,8 @@ silent (each also listed in the design notes):
 * with pad zeroing off, all H lanes are used (the caller guarantees zeros);
 * the GEMM input is NOT rounded to bf16 (full-precision activations);
 * top-k runs on the logits themselves; ties go to the lower index and
-  -0.0 equals +0.0; inputs must be finite;
+  -0.0 equals +0.0; infinities order as numbers; NaN is an error unless the
+  stage-1 fold (``skip_nan_fold`` off) turns it into -inf;
 * page precision (optional, ``page=True`` in ``tail``): the page's own
   numerics, from ``deferred_rms`` (one bf16 rounding of the GEMM input per
   element), ``skip_nan_fold`` (bf16 products summed at full width) and
@@ -127,13 +128,18 @@ def logits(y: np.ndarray, w_bits: np.ndarray, pad: np.ndarray, chunk: int = 8192
 
 
 # ------------------------------------------------------------------- 5. topk
-def topk(L: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
+def topk(L: np.ndarray, k: int, nan_fold: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """Per row, the k largest values, descending; equal values in ascending
-    index order (a full stable sort).  Returns (vals float64 [gbs,k],
-    idx int64 [gbs,k])."""
+    index order (a full stable sort).  Infinities order as numbers (the page,
+    ``skip_nan_fold``: an overflow saturates to +/-inf, which the top-k orders
+    fine).  NaN has no place in that order: it is an error, unless nan_fold,
+    the stage-1 fold that ``skip_nan_fold`` = False keeps, replaces it by -inf
+    (value and rank).  Returns (vals float64 [gbs,k], idx int64 [gbs,k])."""
     L = np.asarray(L, dtype=np.float64)
-    if not np.all(np.isfinite(L)):
-        raise ValueError("top-k input must be finite")
+    if nan_fold:
+        L = np.where(np.isnan(L), -np.inf, L)
+    if np.any(np.isnan(L)):
+        raise ValueError("top-k input must not hold NaN (unless folded)")
     order = np.argsort(-L, axis=1, kind="stable")[:, :k]
     return np.take_along_axis(L, order, axis=1), order.astype(np.int64)
 

@@ -284,3 +284,60 @@ def test_page_tail_within_rounding_bound_of_exact():
         mv, mi = oracle.topk(oracle.mirror(pg["logits"]), k)
         assert np.array_equal(pg["idx"], mi) and np.array_equal(pg["vals"], mv)
         assert np.all((np.asarray(pg["vals"], np.float32).view(np.uint32) & 0xFFFF) == 0)
+
+
+# ------------------------------------------------------------------ NaN fold
+def check_nan_fold(topk) -> list:
+    """The fold ranks NaN (either sign) as -inf and returns -inf for it;
+    infinities order as numbers; brute force by Python's sort."""
+    fails = []
+    rng = np.random.default_rng(17)
+    for trial in range(40):
+        V = int(rng.integers(1, 40))
+        k = int(rng.integers(1, V + 1))
+        L = np.round(rng.standard_normal(V) * 2) / 2
+        L[rng.random(V) < 0.2] = np.nan
+        L[rng.random(V) < 0.1] = -np.nan
+        L[rng.random(V) < 0.1] = np.inf
+        L[rng.random(V) < 0.1] = -np.inf
+        vals, idx = topk(L[None, :], k, nan_fold=True)
+        folded = [(-math.inf if math.isnan(v) else float(v)) for v in L]
+        want = sorted(range(V), key=lambda i: (-folded[i], i))[:k]
+        if list(idx[0]) != want:
+            fails.append(f"trial {trial}: order {list(idx[0])} vs {want}")
+            return fails
+        if not np.array_equal(vals[0], np.array([folded[i] for i in want])):
+            fails.append(f"trial {trial}: values")
+    try:
+        topk(np.array([[1.0, np.nan]]), 1)
+        fails.append("NaN accepted without the fold")
+    except ValueError:
+        pass
+    v, i = topk(np.array([[np.inf, 1.0, -np.inf, 2.0]]), 4)
+    if list(i[0]) != [0, 3, 1, 2]:
+        fails.append("infinities out of order")
+    return fails
+
+
+def test_nan_fold():
+    assert check_nan_fold(oracle.topk) == []
+
+
+@pytest.mark.parametrize("mistake", ["nan_as_zero", "nan_dropped_last", "nan_kept"])
+def test_nan_fold_planted_mistakes_fail(mistake):
+    def bad(L, k, nan_fold=False):
+        L = np.asarray(L, np.float64)
+        if mistake == "nan_as_zero":
+            L = np.where(np.isnan(L), 0.0, L)
+        elif mistake == "nan_dropped_last":  # below -inf, by index order among themselves
+            key = np.where(np.isnan(L), -np.inf, L)
+            order = np.lexsort((np.arange(L.shape[1])[None, :].repeat(L.shape[0], 0),
+                                np.isnan(L), -key), axis=1)[:, :k]
+            return np.take_along_axis(np.where(np.isnan(L), -np.inf, L), order, 1), order
+        else:  # NaN kept as a value that ranks first
+            key = np.where(np.isnan(L), np.inf, L)
+            order = np.argsort(-key, 1, kind="stable")[:, :k]
+            return np.take_along_axis(L, order, 1), order
+        order = np.argsort(-L, 1, kind="stable")[:, :k]
+        return np.take_along_axis(L, order, 1), order
+    assert check_nan_fold(bad)
