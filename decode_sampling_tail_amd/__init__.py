@@ -7,9 +7,10 @@ synchronize.  There is no CPU fallback: if the library is not built, loading
 it raises.
 
 The names mirror the C entry points in include/tail.h:
-rmsnorm, lm_head, rmsnorm_lm_head, topk, topk_mirror, sample, forward,
-workspace_size, status_string.  ``page=True`` selects TAIL_PAGE_PRECISION
-(bf16 GEMM input, top-k over the bf16 logit mirror).
+rmsnorm, lm_head, rmsnorm_lm_head, topk (tail_topk, or tail_topk_ex with its
+options), sample, forward, workspace_size, status_string.  ``page=True``
+selects TAIL_PAGE_PRECISION (bf16 GEMM input, top-k over the bf16 logit
+mirror); ``nan_fold=True`` selects TAIL_NAN_FOLD.
 """
 from __future__ import annotations
 
@@ -21,10 +22,10 @@ LIB_PATH = os.path.join(_HERE, "libtail.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 F32, F16, BF16 = 0, 1, 2
-EMIT_LOGITS, ZERO_PAD, DEFERRED_RMS, PAGE_PRECISION = 1, 2, 4, 8
+EMIT_LOGITS, ZERO_PAD, DEFERRED_RMS, PAGE_PRECISION, NAN_FOLD = 1, 2, 4, 8, 16
 K_MAX, GBS_MAX, H_MAX = 1024, 4096, 65536
 
-EXPORTS = ("tail_rmsnorm", "tail_lm_head", "tail_rmsnorm_lm_head", "tail_topk", "tail_topk_mirror",
+EXPORTS = ("tail_rmsnorm", "tail_lm_head", "tail_rmsnorm_lm_head", "tail_topk", "tail_topk_ex",
            "tail_sample", "tail_forward", "tail_workspace_size", "tail_status_string")
 
 _lib = None
@@ -48,7 +49,7 @@ def lib() -> ctypes.CDLL:
         L.tail_lm_head.argtypes = [vp, vp, vp, i, i, i, i, u, vp, vp, sz, vp]
         L.tail_rmsnorm_lm_head.argtypes = [vp, i, vp, vp, i, i, i, i, f, u, vp, vp, vp, sz, vp]
         L.tail_topk.argtypes = [vp, i, i, i, vp, vp, vp, sz, vp]
-        L.tail_topk_mirror.argtypes = [vp, i, i, i, vp, vp, vp, sz, vp]
+        L.tail_topk_ex.argtypes = [vp, i, i, i, u, vp, vp, vp, vp, sz, vp]
         L.tail_sample.argtypes = [vp, vp, i, i, vp, i, vp, vp]
         L.tail_forward.argtypes = [vp, i, vp, vp, i, i, i, i, i, f, u, vp, i, vp, vp, vp, vp, vp, sz, vp]
         L.tail_workspace_size.argtypes = [i, i, i, i, i, u]
@@ -56,7 +57,7 @@ def lib() -> ctypes.CDLL:
         L.tail_status_string.argtypes = [i]
         L.tail_status_string.restype = ctypes.c_char_p
         for name in ("tail_rmsnorm", "tail_lm_head", "tail_rmsnorm_lm_head", "tail_topk",
-                     "tail_topk_mirror", "tail_sample", "tail_forward"):
+                     "tail_topk_ex", "tail_sample", "tail_forward"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -116,9 +117,10 @@ def _call(name, *args):
         raise TailError(name, st)
 
 
-def _flags(zero_pad=False, deferred=False, emit=False, page=False) -> int:
+def _flags(zero_pad=False, deferred=False, emit=False, page=False, nan_fold=False) -> int:
     return ((ZERO_PAD if zero_pad else 0) | (DEFERRED_RMS if deferred else 0) |
-            (EMIT_LOGITS if emit else 0) | (PAGE_PRECISION if page else 0))
+            (EMIT_LOGITS if emit else 0) | (PAGE_PRECISION if page else 0) |
+            (NAN_FOLD if nan_fold else 0))
 
 
 def rmsnorm(hidden, gamma, H_u=None, eps=1e-5, zero_pad=False, deferred=False, out_y=None, out_r=None,
@@ -170,9 +172,11 @@ def rmsnorm_lm_head(hidden, gamma, w_t, H_u=None, eps=1e-5, zero_pad=False, defe
     return logits, r
 
 
-def topk(logits, k, out_vals=None, out_idx=None, ws=None, mirror=False):
-    """tail_topk (or tail_topk_mirror: ranks the bf16 rounding of the
-    logits): (vals [gbs,k] fp32 descending, idx [gbs,k] int32)."""
+def topk(logits, k, out_vals=None, out_idx=None, ws=None, mirror=False, nan_fold=False, taps=None):
+    """tail_topk, or tail_topk_ex when mirror (rank the bf16 rounding of the
+    logits), nan_fold (NaN ranks as -inf) or taps ([gbs, 4] int32 tensor for
+    the stage-1 diagnostics, as raw u32) is given: (vals [gbs,k] fp32
+    descending, idx [gbs,k] int32)."""
     torch = _torch()
     dev = _dev(logits)
     gbs, V = logits.shape
@@ -180,8 +184,13 @@ def topk(logits, k, out_vals=None, out_idx=None, ws=None, mirror=False):
     idx = out_idx if out_idx is not None else torch.empty((gbs, k), dtype=torch.int32, device=dev)
     if ws is None:
         ws = torch.empty(max(workspace_size(gbs, 1, 1, V, k, EMIT_LOGITS), 1), dtype=torch.uint8, device=dev)
-    _call("tail_topk_mirror" if mirror else "tail_topk", _ptr(logits), gbs, V, k, _ptr(vals), _ptr(idx),
-          _ptr(ws), ws.numel(), _stream(dev))
+    if mirror or nan_fold or taps is not None:
+        flags = (PAGE_PRECISION if mirror else 0) | (NAN_FOLD if nan_fold else 0)
+        _call("tail_topk_ex", _ptr(logits), gbs, V, k, flags, _ptr(vals), _ptr(idx), _ptr(taps),
+              _ptr(ws), ws.numel(), _stream(dev))
+    else:
+        _call("tail_topk", _ptr(logits), gbs, V, k, _ptr(vals), _ptr(idx), _ptr(ws), ws.numel(),
+              _stream(dev))
     return vals, idx
 
 
@@ -201,12 +210,12 @@ class Forward:
     fixed shapes (what a decode loop or a benchmark wants)."""
 
     def __init__(self, gbs, H, V, k=256, H_u=None, eps=1e-5, zero_pad=False, deferred=True,
-                 emit_logits=True, device="cuda", page=False):
+                 emit_logits=True, device="cuda", page=False, nan_fold=False):
         torch = _torch()
         self.gbs, self.H, self.V, self.k = gbs, H, V, k
         self.H_u = H if H_u is None else H_u
         self.eps = eps
-        self.flags = _flags(zero_pad, deferred, emit_logits, page)
+        self.flags = _flags(zero_pad, deferred, emit_logits, page, nan_fold)
         self.device = torch.device(device)
         dev = self.device
         self.logits = torch.empty((gbs, V), dtype=torch.float32, device=dev) if emit_logits else None

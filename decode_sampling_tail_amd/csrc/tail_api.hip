@@ -12,8 +12,11 @@ namespace {
 
 using tail::align256;
 
-constexpr unsigned kAllFlags =
+// flags each entry accepts (any other bit is TAIL_ERR_INVALID_ARG)
+constexpr unsigned kNormFlags =
     TAIL_EMIT_LOGITS | TAIL_ZERO_PAD | TAIL_DEFERRED_RMS | TAIL_PAGE_PRECISION;
+constexpr unsigned kAllFlags = kNormFlags | TAIL_NAN_FOLD;
+constexpr unsigned kTopkFlags = TAIL_PAGE_PRECISION | TAIL_NAN_FOLD;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -159,7 +162,7 @@ TAIL_API int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int
   if (int s = check_shape(gbs, H, H_u)) return s;
   if (dtype != TAIL_F32 && dtype != TAIL_F16 && dtype != TAIL_BF16) return TAIL_ERR_INVALID_ARG;
   if (!(eps >= 0.0f) || !isfinite(eps)) return TAIL_ERR_INVALID_ARG;
-  if (flags & ~kAllFlags) return TAIL_ERR_INVALID_ARG;
+  if (flags & ~kNormFlags) return TAIL_ERR_INVALID_ARG;
   int ps = pad_stride(H, H_u, flags);
   if (ps < 0) return TAIL_ERR_INVALID_ARG;
   bool deferred = flags & TAIL_DEFERRED_RMS;
@@ -177,7 +180,7 @@ TAIL_API int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_
                           size_t ws_bytes, void* stream) {
   if (int s = check_shape(gbs, H, H_u)) return s;
   if (int s = check_vocab(V)) return s;
-  if (flags & ~kAllFlags) return TAIL_ERR_INVALID_ARG;
+  if (flags & ~kNormFlags) return TAIL_ERR_INVALID_ARG;
   int ps = pad_stride(H, H_u, flags);
   if (ps < 0) return TAIL_ERR_INVALID_ARG;
   if (!y || !w_t || !logits) return TAIL_ERR_INVALID_ARG;
@@ -207,7 +210,7 @@ TAIL_API int tail_rmsnorm_lm_head(const void* hidden, int dtype, const float* ga
   if (int s = check_vocab(V)) return s;
   if (dtype != TAIL_F32 && dtype != TAIL_F16 && dtype != TAIL_BF16) return TAIL_ERR_INVALID_ARG;
   if (!(eps >= 0.0f) || !isfinite(eps)) return TAIL_ERR_INVALID_ARG;
-  if (flags & ~kAllFlags) return TAIL_ERR_INVALID_ARG;
+  if (flags & ~kNormFlags) return TAIL_ERR_INVALID_ARG;
   const int ps = pad_stride(H, H_u, flags);
   if (ps < 0) return TAIL_ERR_INVALID_ARG;
   if (!hidden || !gamma || !w_t || !logits) return TAIL_ERR_INVALID_ARG;
@@ -225,30 +228,33 @@ TAIL_API int tail_rmsnorm_lm_head(const void* hidden, int dtype, const float* ga
 }
 
 namespace {
-int topk_call(const float* logits, int gbs, int V, int k, bool mirror, float* vals, int32_t* idx,
-              void* ws, size_t ws_bytes, void* stream) {
+int topk_call(const float* logits, int gbs, int V, int k, unsigned flags, float* vals, int32_t* idx,
+              uint32_t* taps, void* ws, size_t ws_bytes, void* stream) {
+  if (flags & ~kTopkFlags) return TAIL_ERR_INVALID_ARG;
   if (gbs < 1) return TAIL_ERR_INVALID_ARG;
   if (gbs > TAIL_GBS_MAX) return TAIL_ERR_UNSUPPORTED;
   if (int s = check_vocab(V)) return s;
   if (int s = check_k(V, k)) return s;
   if (!logits || !vals || !idx) return TAIL_ERR_INVALID_ARG;
-  if (!aligned(logits, 16) || !aligned(vals, 4) || !aligned(idx, 4)) return TAIL_ERR_INVALID_ARG;
+  if (!aligned(logits, 16) || !aligned(vals, 4) || !aligned(idx, 4) || (taps && !aligned(taps, 4)))
+    return TAIL_ERR_INVALID_ARG;
   if (int s = check_ws(ws, ws_bytes, topk_ws_bytes(gbs, V, k))) return s;
   tail::TopkGeom g;
   tail::topk_geometry(V, k, &g);
-  return hip_status(tail::launch_topk(logits, gbs, V, k, g, (uint32_t*)ws, mirror, vals, idx,
-                                      (hipStream_t)stream));
+  return hip_status(tail::launch_topk(logits, gbs, V, k, g, (uint32_t*)ws,
+                                      flags & TAIL_PAGE_PRECISION, flags & TAIL_NAN_FOLD, vals, idx,
+                                      taps, (hipStream_t)stream));
 }
 }  // namespace
 
 TAIL_API int tail_topk(const float* logits, int gbs, int V, int k, float* vals, int32_t* idx,
                        void* ws, size_t ws_bytes, void* stream) {
-  return topk_call(logits, gbs, V, k, false, vals, idx, ws, ws_bytes, stream);
+  return topk_call(logits, gbs, V, k, 0u, vals, idx, nullptr, ws, ws_bytes, stream);
 }
 
-TAIL_API int tail_topk_mirror(const float* logits, int gbs, int V, int k, float* vals,
-                              int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  return topk_call(logits, gbs, V, k, true, vals, idx, ws, ws_bytes, stream);
+TAIL_API int tail_topk_ex(const float* logits, int gbs, int V, int k, unsigned flags, float* vals,
+                          int32_t* idx, uint32_t* taps, void* ws, size_t ws_bytes, void* stream) {
+  return topk_call(logits, gbs, V, k, flags, vals, idx, taps, ws, ws_bytes, stream);
 }
 
 TAIL_API int tail_sample(const float* vals, const int32_t* idx, int gbs, int k,
@@ -297,14 +303,16 @@ TAIL_API int tail_forward(const void* hidden, int dtype, const float* gamma, con
   tail::TopkGeom g;
   tail::topk_geometry(V, k, &g);
   // group maxima come from the lm_head epilogue when the top-k groups are its
-  // 64-column groups; otherwise from a separate pass over the logits
-  const bool fused_groups = g.gs == tail::kFusedGroup;
+  // 64-column groups; otherwise (or with the NaN fold) from a separate pass
+  // over the logits
+  const bool fold = flags & TAIL_NAN_FOLD;
+  const bool fused_groups = g.gs == tail::kFusedGroup && !fold;
   uint32_t* gk_fused = fused_groups ? gk : nullptr;
   hipError_t e = norm_lm_head(hidden, dtype, gamma, w_t, gbs, H, H_u, V, eps, ps, flags, y, r, act,
                               lg, gk_fused, st);
-  if (e == hipSuccess && !fused_groups) e = tail::launch_group_max(lg, gbs, V, g, gk, st);
+  if (e == hipSuccess && !fused_groups) e = tail::launch_group_max(lg, gbs, V, g, fold, gk, st);
   if (e == hipSuccess)
-    e = tail::launch_select(lg, gbs, V, k, g, gk, flags & TAIL_PAGE_PRECISION, vals, idx, params,
-                            ncols, tokens, st);
+    e = tail::launch_select(lg, gbs, V, k, g, gk, flags & TAIL_PAGE_PRECISION, fold, vals, idx,
+                            nullptr, params, ncols, tokens, st);
   return hip_status(e);
 }

@@ -126,19 +126,24 @@ hipError_t launch_lm_head_mfma(const uint16_t* act, int nt, int rows_pad, int Kp
                                int V, int H_u, int pad_s, const float* row_scale, int gbs,
                                float* logits, uint32_t* gkey, hipStream_t st);
 
-hipError_t launch_group_max(const float* logits, int gbs, int V, const TopkGeom& geom,
+// fold: NaN counts as -inf (the page's stage-1 NaN fold)
+hipError_t launch_group_max(const float* logits, int gbs, int V, const TopkGeom& geom, bool fold,
                             uint32_t* gkey, hipStream_t st);
 
 // params NULL: no sampling (ncols and tokens unused).  mirror: rank the bf16
 // rounding of every logit and return the rounded values (gkey may hold the
 // unrounded group maxima: rounding is monotone, so the rounded maximum is the
-// maximum of the rounded values).
+// maximum of the rounded values).  fold: NaN ranks and is returned as -inf
+// (gkey must then be computed with the same fold).  taps (may be NULL): 4 u32
+// stage-1 diagnostics per row.
 hipError_t launch_select(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
-                         const uint32_t* gkey, bool mirror, float* vals, int32_t* idx,
-                         const float* params, int ncols, int32_t* tokens, hipStream_t st);
+                         const uint32_t* gkey, bool mirror, bool fold, float* vals, int32_t* idx,
+                         uint32_t* taps, const float* params, int ncols, int32_t* tokens,
+                         hipStream_t st);
 
 hipError_t launch_topk(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
-                       uint32_t* gkey_ws, bool mirror, float* vals, int32_t* idx, hipStream_t st);
+                       uint32_t* gkey_ws, bool mirror, bool fold, float* vals, int32_t* idx,
+                       uint32_t* taps, hipStream_t st);
 
 hipError_t launch_sample(const float* vals, const int32_t* idx, int gbs, int k,
                          const float* params, int ncols, int32_t* tokens, hipStream_t st);

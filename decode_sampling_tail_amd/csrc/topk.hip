@@ -36,6 +36,17 @@
 // returned.  The group maxima may come from the unrounded logits: rounding
 // is monotone, so the rounded maximum of a group is the maximum of its
 // rounded elements, and step a's bound holds unchanged.
+//
+// NaN fold (parameter "skip_nan_fold" off): a NaN logit (either sign) ranks
+// and is returned as -inf; the group maxima must then come from
+// group_max_kernel with the same fold (a NaN in the lm_head epilogue's
+// maxima would hide its group's real maximum).  Without the fold, NaN
+// ordering is unspecified; infinities always order as numbers.
+//
+// Taps (optional, per row, 4 x u32): the bound t0 as an order-preserving key,
+// the number of candidate groups, the number of elements with key >= t0 (all
+// of them, also past the LDS capacity), and 1 when that number exceeded the
+// capacity (the radix path of step e ran), else 0.
 #include "sampler_row.h"
 #include "../../include/tail.h"
 
@@ -57,8 +68,14 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+__device__ inline uint32_t fold_key(float f, int fold) {
+  uint32_t u = __float_as_uint(f);
+  if (fold && (u & 0x7FFFFFFFu) > 0x7F800000u) u = 0xFF800000u;  // NaN -> -inf
+  return float_key(__uint_as_float(u));
+}
+
 __global__ __launch_bounds__(kGmThreads) void group_max_kernel(const float* __restrict__ logits,
-                                                               int V, int gs, int groups,
+                                                               int V, int gs, int groups, int fold,
                                                                uint32_t* __restrict__ gkey) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = blockIdx.x * (kGmThreads / 64) + wave;
@@ -72,10 +89,11 @@ __global__ __launch_bounds__(kGmThreads) void group_max_kernel(const float* __re
     const float4* p4 = reinterpret_cast<const float4*>(p);
     for (int i = lane; i < n / 4; i += 64) {
       float4 v = p4[i];
-      m = max(m, max(max(float_key(v.x), float_key(v.y)), max(float_key(v.z), float_key(v.w))));
+      m = max(m, max(max(fold_key(v.x, fold), fold_key(v.y, fold)),
+                     max(fold_key(v.z, fold), fold_key(v.w, fold))));
     }
   } else {
-    for (int i = lane; i < n; i += 64) m = max(m, float_key(p[i]));
+    for (int i = lane; i < n; i += 64) m = max(m, fold_key(p[i], fold));
   }
   m = wave_max_u32(m);
   if (lane == 0) gkey[size_t(row) * groups + g] = m;
@@ -216,9 +234,11 @@ __device__ inline void wave_append(SelShared& s, bool pred, uint32_t key, int e,
 // The bits an element is ranked and returned by: its own, or (mirror) its
 // bf16 rounding.
 template <bool MIRROR>
-__device__ inline uint32_t rank_bits(float x) {
-  if constexpr (MIRROR) return bf16_rne_bits(__float_as_uint(x)) << 16;
-  else return __float_as_uint(x);
+__device__ inline uint32_t rank_bits(float x, bool fold) {
+  uint32_t u = __float_as_uint(x);
+  if (fold && (u & 0x7FFFFFFFu) > 0x7F800000u) u = 0xFF800000u;  // NaN -> -inf
+  if constexpr (MIRROR) return bf16_rne_bits(u) << 16;
+  else return u;
 }
 
 // Order-preserving key -> the key of the value's bf16 rounding.
@@ -232,7 +252,7 @@ __device__ inline uint32_t mirror_key(uint32_t key) {
 // number of times (out-of-range slots have in == false).
 template <bool MIRROR, typename F>
 __device__ inline void for_candidates(const SelShared& s, const float* row, int V, int gs, int nact,
-                                      int tid, F&& f) {
+                                      int tid, bool fold, F&& f) {
   const int wave_first = tid & ~63;
   if (gs >= 4) {
     const int per = gs >> 2;  // float4 items per group (a power of two)
@@ -256,8 +276,8 @@ __device__ inline void for_candidates(const SelShared& s, const float* row, int 
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        const uint32_t bx = rank_bits<MIRROR>(v[u].x), by = rank_bits<MIRROR>(v[u].y);
-        const uint32_t bz = rank_bits<MIRROR>(v[u].z), bw = rank_bits<MIRROR>(v[u].w);
+        const uint32_t bx = rank_bits<MIRROR>(v[u].x, fold), by = rank_bits<MIRROR>(v[u].y, fold);
+        const uint32_t bz = rank_bits<MIRROR>(v[u].z, fold), bw = rank_bits<MIRROR>(v[u].w, fold);
         f(in[u], float_key(__uint_as_float(bx)), e[u], bx);
         f(in[u], float_key(__uint_as_float(by)), e[u] + 1, by);
         f(in[u], float_key(__uint_as_float(bz)), e[u] + 2, bz);
@@ -274,7 +294,7 @@ __device__ inline void for_candidates(const SelShared& s, const float* row, int 
         e = int(s.act[fi / gs]) * gs + fi % gs;
         in = e < V;
       }
-      const uint32_t bx = rank_bits<MIRROR>(in ? row[e] : 0.0f);
+      const uint32_t bx = rank_bits<MIRROR>(in ? row[e] : 0.0f, fold);
       f(in, float_key(__uint_as_float(bx)), e, bx);
     }
   }
@@ -283,8 +303,9 @@ __device__ inline void for_candidates(const SelShared& s, const float* row, int 
 template <int P, bool MIRROR>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ logits, int V, int gs, int groups, int k,
-    const uint32_t* __restrict__ gkey, float* __restrict__ vals, int32_t* __restrict__ idx,
-    const float* __restrict__ params, int ncols, int32_t* __restrict__ tokens) {
+    const uint32_t* __restrict__ gkey, int fold, float* __restrict__ vals,
+    int32_t* __restrict__ idx, uint32_t* __restrict__ taps, const float* __restrict__ params,
+    int ncols, int32_t* __restrict__ tokens) {
   __shared__ SelShared s;
   const int tid = threadIdx.x, lane = tid & 63;
   const int row_id = blockIdx.x;
@@ -370,17 +391,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int nact = int(s.nact);
 
   // b. every element >= t0
-  for_candidates<MIRROR>(s, row, V, gs, nact, tid,
+  for_candidates<MIRROR>(s, row, V, gs, nact, tid, fold != 0,
                  [&](bool in, uint32_t key, int e, uint32_t bits) {
                    wave_append(s, in && key >= t0, key, e, bits, lane);
                  });
   __syncthreads();
   uint32_t n = s.cnt;
+  if (taps != nullptr && tid == 0) {
+    uint32_t* tp = taps + size_t(row_id) * 4;
+    tp[0] = t0;
+    tp[1] = uint32_t(nact);
+    tp[2] = n;
+    tp[3] = n > uint32_t(kCap) ? 1u : 0u;
+  }
 
   // e. too many: find the cut by radix passes over the candidate groups
   if (n > uint32_t(kCap)) {
     auto visit_all = [&](auto&& f) {
-      for_candidates<MIRROR>(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int, uint32_t) {
+      for_candidates<MIRROR>(s, row, V, gs, nact, tid, fold != 0, [&](bool in, uint32_t key, int, uint32_t) {
         if (in && key >= t0) f(key);
       });
     };
@@ -389,7 +417,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (above + equal > uint32_t(kCap)) {
       uint32_t a2, e2;
       const uint32_t nk = radix_kth(s, tid, uint32_t(k) - above, [&](auto&& f) {
-        for_candidates<MIRROR>(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int e, uint32_t) {
+        for_candidates<MIRROR>(s, row, V, gs, nact, tid, fold != 0, [&](bool in, uint32_t key, int e, uint32_t) {
           if (in && key == vstar) f(~uint32_t(e));
         });
       }, &a2, &e2);
@@ -398,7 +426,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __syncthreads();
     if (tid == 0) s.cnt = 0;
     __syncthreads();
-    for_candidates<MIRROR>(s, row, V, gs, nact, tid, [&](bool in, uint32_t key, int e, uint32_t bits) {
+    for_candidates<MIRROR>(s, row, V, gs, nact, tid, fold != 0, [&](bool in, uint32_t key, int e, uint32_t bits) {
       wave_append(s, in && (key > vstar || (key == vstar && e <= ecut)), key, e, bits, lane);
     });
     __syncthreads();
@@ -547,24 +575,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
 }  // namespace
 
-hipError_t launch_group_max(const float* logits, int gbs, int V, const TopkGeom& geom,
+hipError_t launch_group_max(const float* logits, int gbs, int V, const TopkGeom& geom, bool fold,
                             uint32_t* gkey, hipStream_t st) {
   const int gpb = kGmThreads / 64;
   dim3 g1((geom.groups + gpb - 1) / gpb, gbs);
   hipLaunchKernelGGL(group_max_kernel, g1, dim3(kGmThreads), 0, st, logits, V, geom.gs, geom.groups,
-                     gkey);
+                     int(fold), gkey);
   return hipGetLastError();
 }
 
 namespace {
 template <bool MIRROR>
 void select_dispatch(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
-                     const uint32_t* gkey, float* vals, int32_t* idx, const float* params,
-                     int ncols, int32_t* tokens, hipStream_t st) {
+                     const uint32_t* gkey, bool fold, float* vals, int32_t* idx, uint32_t* taps,
+                     const float* params, int ncols, int32_t* tokens, hipStream_t st) {
   dim3 grid(gbs), block(kSelThreads);
 #define TAIL_SELECT_LAUNCH(P)                                                                  \
   hipLaunchKernelGGL((select_kernel<P, MIRROR>), grid, block, 0, st, logits, V, geom.gs,       \
-                     geom.groups, k, gkey, vals, idx, params, ncols, tokens)
+                     geom.groups, k, gkey, int(fold), vals, idx, taps, params, ncols, tokens)
   if (k <= 64) TAIL_SELECT_LAUNCH(1);
   else if (k <= 128) TAIL_SELECT_LAUNCH(2);
   else if (k <= 256) TAIL_SELECT_LAUNCH(4);
@@ -575,21 +603,25 @@ void select_dispatch(const float* logits, int gbs, int V, int k, const TopkGeom&
 }  // namespace
 
 hipError_t launch_select(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
-                         const uint32_t* gkey, bool mirror, float* vals, int32_t* idx,
-                         const float* params, int ncols, int32_t* tokens, hipStream_t st) {
+                         const uint32_t* gkey, bool mirror, bool fold, float* vals, int32_t* idx,
+                         uint32_t* taps, const float* params, int ncols, int32_t* tokens,
+                         hipStream_t st) {
   if (mirror)
-    select_dispatch<true>(logits, gbs, V, k, geom, gkey, vals, idx, params, ncols, tokens, st);
+    select_dispatch<true>(logits, gbs, V, k, geom, gkey, fold, vals, idx, taps, params, ncols,
+                          tokens, st);
   else
-    select_dispatch<false>(logits, gbs, V, k, geom, gkey, vals, idx, params, ncols, tokens, st);
+    select_dispatch<false>(logits, gbs, V, k, geom, gkey, fold, vals, idx, taps, params, ncols,
+                           tokens, st);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, int gbs, int V, int k, const TopkGeom& geom,
-                       uint32_t* gkey_ws, bool mirror, float* vals, int32_t* idx, hipStream_t st) {
-  hipError_t e = launch_group_max(logits, gbs, V, geom, gkey_ws, st);
+                       uint32_t* gkey_ws, bool mirror, bool fold, float* vals, int32_t* idx,
+                       uint32_t* taps, hipStream_t st) {
+  hipError_t e = launch_group_max(logits, gbs, V, geom, fold, gkey_ws, st);
   if (e != hipSuccess) return e;
-  return launch_select(logits, gbs, V, k, geom, gkey_ws, mirror, vals, idx, nullptr, 0, nullptr,
-                       st);
+  return launch_select(logits, gbs, V, k, geom, gkey_ws, mirror, fold, vals, idx, taps, nullptr, 0,
+                       nullptr, st);
 }
 
 }  // namespace tail

@@ -52,6 +52,10 @@ extern "C" {
 #define TAIL_ZERO_PAD 2u     /* "zero_interleaved_pad": skip the interleaved pad lanes */
 #define TAIL_DEFERRED_RMS 4u /* "deferred_rms": apply the row's rms scale after the contraction */
 #define TAIL_PAGE_PRECISION 8u /* the page's own numerics (below) */
+#define TAIL_NAN_FOLD 16u      /* "skip_nan_fold" off: NaN logits rank (and return) as -inf */
+/* Each entry point rejects (TAIL_ERR_INVALID_ARG) the bits it does not accept:
+ * tail_rmsnorm, tail_lm_head and tail_rmsnorm_lm_head take the first four,
+ * tail_forward all five, tail_topk_ex TAIL_PAGE_PRECISION and TAIL_NAN_FOLD. */
 
 /* limits of this build */
 #define TAIL_K_MAX 1024      /* largest k ("k": 256 in production) */
@@ -163,15 +167,30 @@ int tail_topk(const float* logits, int gbs, int V, int k, float* vals, int32_t* 
               size_t ws_bytes, void* stream);
 
 /*
- * tail_topk_mirror -- the same over the bf16 mirror of the logits ("emit_logits":
- * the page's top-k ranks the bf16 copy of the fp32 logits): every logit is
- * rounded to bf16 (nearest, ties to even) before ranking, and vals receives
- * the rounded values (fp32 with zero low 16 bits).  Distinct logits that round
- * to the same bf16 tie, and ties keep the lower indices.  Arguments and
- * workspace as for tail_topk.
+ * tail_topk_ex -- tail_topk with the page's top-k options ("emit_logits",
+ * "skip_nan_fold", "debug_taps").  Arguments and workspace as for tail_topk;
+ * infinities always order as numbers.
+ *   flags: TAIL_PAGE_PRECISION ranks the bf16 mirror of the logits (each logit
+ *          rounded to bf16, nearest, ties to even) and returns the rounded
+ *          values (fp32 with zero low 16 bits); distinct logits that round to
+ *          one bf16 tie, and ties keep the lower indices.
+ *          TAIL_NAN_FOLD ranks a NaN logit (either sign) as -inf and returns
+ *          -inf for it (without it, NaN ordering is unspecified).  Any other
+ *          bit is TAIL_ERR_INVALID_ARG.
+ *   taps:  [gbs, 4] u32 or NULL ("debug_taps": the page does not list its
+ *          taps; these are this top-k's stage-1 diagnostics): per row, the
+ *          lower bound t0 of the k-th largest group maximum as an
+ *          order-preserving key (key(f) = bits | 0x80000000 for f >= +0,
+ *          ~bits for f < 0, -0.0 as +0.0; the same transform applies to the
+ *          mirrored and folded values the row is ranked by), the number of
+ *          candidate groups (gs consecutive columns, gs the largest power of
+ *          two <= 64 that leaves at least k groups, doubled while there are
+ *          more than 8192) whose maximum key is >= t0, the number of elements
+ *          with key >= t0, and 1 if that number exceeded 4096 (the exact
+ *          multi-pass path ran) or 0.
  */
-int tail_topk_mirror(const float* logits, int gbs, int V, int k, float* vals, int32_t* idx,
-                     void* ws, size_t ws_bytes, void* stream);
+int tail_topk_ex(const float* logits, int gbs, int V, int k, unsigned flags, float* vals,
+                 int32_t* idx, uint32_t* taps, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * tail_sample -- per-row sampler over the k candidates ("sampling_params").
@@ -197,7 +216,10 @@ int tail_sample(const float* vals, const int32_t* idx, int gbs, int k, const flo
  *
  *   hidden, dtype, gamma, w_t, gbs, H, H_u, V, k, eps: as above.
  *   flags:  TAIL_EMIT_LOGITS (write `logits`), TAIL_ZERO_PAD, TAIL_DEFERRED_RMS,
- *           TAIL_PAGE_PRECISION (bf16 GEMM input and the top-k of tail_topk_mirror).
+ *           TAIL_PAGE_PRECISION (bf16 GEMM input, and the top-k ranks the bf16
+ *           mirror as tail_topk_ex does), TAIL_NAN_FOLD (the top-k folds NaN
+ *           logits to -inf as tail_topk_ex does; NaN-free logits give the same
+ *           outputs either way).  A row with no finite logit has no defined token.
  *   params: [gbs, ncols] or NULL; NULL skips the sampler and leaves `tokens`
  *           untouched (tokens may then be NULL).
  *   logits: [gbs, V] fp32, required only with TAIL_EMIT_LOGITS.

@@ -46,6 +46,7 @@ def test_header_constants_match_binding():
     assert int(consts["TAIL_DEFERRED_RMS"]) == dst.DEFERRED_RMS
     assert int(consts["TAIL_EMIT_LOGITS"]) == dst.EMIT_LOGITS
     assert int(consts["TAIL_PAGE_PRECISION"]) == dst.PAGE_PRECISION
+    assert int(consts["TAIL_NAN_FOLD"]) == dst.NAN_FOLD
     assert int(consts["TAIL_K_MAX"]) == dst.K_MAX
 
 
@@ -131,37 +132,53 @@ def test_rmsnorm_lm_head_validation():
     assert rlh(eps=-1.0) == E
     assert rlh(H_u=2881) == E
     assert rlh(gbs=0) == E
-    assert rlh(flags=16) == E
+    assert rlh(flags=16) == E                                 # the NaN fold is a top-k option
+    assert rlh(flags=32) == E
     assert rlh(w=ctypes.c_void_p(0x100008)) == E
     assert rlh(V=100) == dst.ERR_UNSUPPORTED
     assert rlh(ws=NULL) == dst.ERR_WORKSPACE
     assert rlh(gbs=64, ws_bytes=1024) == dst.ERR_WORKSPACE   # matrix-core activations need room
 
 
-def tk(mirror=False, **kw):
-    a = dict(logits=P, gbs=2, V=4096, k=16, vals=P, idx=P, ws=P, ws_bytes=1 << 20)
+def tk(ex=False, **kw):
+    a = dict(logits=P, gbs=2, V=4096, k=16, vals=P, idx=P, ws=P, ws_bytes=1 << 20, flags=0, taps=None)
     a.update(kw)
-    fn = dst.lib().tail_topk_mirror if mirror else dst.lib().tail_topk
-    return fn(a["logits"], a["gbs"], a["V"], a["k"], a["vals"], a["idx"], a["ws"], a["ws_bytes"], None)
+    if ex:
+        return dst.lib().tail_topk_ex(a["logits"], a["gbs"], a["V"], a["k"], a["flags"], a["vals"],
+                                      a["idx"], a["taps"], a["ws"], a["ws_bytes"], None)
+    return dst.lib().tail_topk(a["logits"], a["gbs"], a["V"], a["k"], a["vals"], a["idx"], a["ws"],
+                               a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("mirror", [False, True])
 def test_topk_validation(mirror):
+    """tail_topk and tail_topk_ex share the validation (mirror=True runs the
+    latter, with its flags and a taps pointer)."""
     E = dst.ERR_INVALID_ARG
-    assert tk(mirror, k=0) == E
-    assert tk(mirror, k=4097) == E                                      # k > V
-    assert tk(mirror, V=8192, k=dst.K_MAX + 1) == dst.ERR_UNSUPPORTED
-    assert tk(mirror, gbs=0) == E
-    assert tk(mirror, logits=NULL) == E
-    assert tk(mirror, vals=NULL) == E
-    assert tk(mirror, idx=NULL) == E
-    assert tk(mirror, V=4100) == dst.ERR_UNSUPPORTED
-    assert tk(mirror, ws=NULL) == dst.ERR_WORKSPACE
-    assert tk(mirror, ws=ctypes.c_void_p(0x100010)) == dst.ERR_WORKSPACE
+    assert tk(mirror, flags=dst.PAGE_PRECISION if mirror else 0, k=0) == E
+    assert tk(mirror, flags=dst.PAGE_PRECISION if mirror else 0, k=4097) == E                                      # k > V
+    assert tk(mirror, flags=dst.PAGE_PRECISION if mirror else 0, V=8192, k=dst.K_MAX + 1) == dst.ERR_UNSUPPORTED
+    assert tk(mirror, flags=dst.PAGE_PRECISION if mirror else 0, gbs=0) == E
+    assert tk(mirror, flags=dst.PAGE_PRECISION if mirror else 0, logits=NULL) == E
+    assert tk(mirror, flags=dst.PAGE_PRECISION if mirror else 0, vals=NULL) == E
+    assert tk(mirror, flags=dst.PAGE_PRECISION if mirror else 0, idx=NULL) == E
+    assert tk(mirror, flags=dst.PAGE_PRECISION if mirror else 0, V=4100) == dst.ERR_UNSUPPORTED
+    assert tk(mirror, flags=dst.PAGE_PRECISION if mirror else 0, ws=NULL) == dst.ERR_WORKSPACE
+    assert tk(mirror, flags=dst.PAGE_PRECISION if mirror else 0, ws=ctypes.c_void_p(0x100010)) == dst.ERR_WORKSPACE
     # 16 groups of 256 columns per row: 2 rows * 16 * 4 bytes of group maxima, in
     # one 256-byte aligned block
-    assert tk(mirror, ws_bytes=255) == dst.ERR_WORKSPACE
+    assert tk(mirror, flags=dst.PAGE_PRECISION if mirror else 0, ws_bytes=255) == dst.ERR_WORKSPACE
     assert dst.workspace_size(2, 1, 1, 4096, 16, dst.EMIT_LOGITS) >= 256
+
+
+def test_topk_ex_flags():
+    E = dst.ERR_INVALID_ARG
+    for f in (0, dst.PAGE_PRECISION, dst.NAN_FOLD, dst.PAGE_PRECISION | dst.NAN_FOLD):
+        assert tk(True, flags=f, logits=NULL) == E          # validation reached past the flags
+        assert tk(True, flags=f, taps=P, ws=NULL) == dst.ERR_WORKSPACE
+    for f in (dst.EMIT_LOGITS, dst.ZERO_PAD, dst.DEFERRED_RMS, 32, 1 << 31):
+        assert tk(True, flags=f) == E                       # not a top-k option
+    assert tk(True, taps=P2) == E                           # taps must be 4-byte aligned
 
 
 def smp(**kw):
@@ -203,7 +220,7 @@ def test_forward_validation():
     assert fwd(w=NULL) == E
     assert fwd(dtype=7) == E
     assert fwd(k=257, V=256) == E
-    assert fwd(H=3072, H_u=2880, flags=dst.ZERO_PAD | 16) == E  # unknown flag bit
+    assert fwd(H=3072, H_u=2880, flags=dst.ZERO_PAD | 32) == E  # unknown flag bit
     assert fwd(ws=NULL) == dst.ERR_WORKSPACE
     need = dst.workspace_size(8, 2880, 2880, 201088, 256, dst.EMIT_LOGITS)
     assert fwd(ws_bytes=need - 1) == dst.ERR_WORKSPACE
