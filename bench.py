@@ -11,7 +11,8 @@ bf16 hidden, sampling at top_k 256, top_p 1, T 1, u 0.5, logits not emitted.
 the stream the library launches on, bracketed by device synchronizations.
 
 Also reported: per-step p10/p50/p90, the step with logits emitted, per-stage
-times, the page-precision mode's step and lm_head (`page_precision`), the lm_head kernel's algorithmic HBM rate against the 8 TB/s peak
+times, the page-precision mode's step and lm_head (`page_precision`), the
+step on one vocabulary shard's shape (V / 8 columns, `vocab_shard_points`), the lm_head kernel's algorithmic HBM rate against the 8 TB/s peak
 (`roofline`), the same numbers at gbs 8 / 64 / 256 (`by_gbs`, with the
 matrix-core kernels' executed TFLOP/s against the 2.5 PFLOP/s dense bf16
 peak), and the fp64 CPU oracle timed on a bounded sample of the headline
@@ -51,6 +52,7 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="headline workload only")
     ap.add_argument("--workload", default=None,
                     help="time only this workload label (for per-workload profiling runs)")
+    ap.add_argument("--no-shard", action="store_true", help="skip the vocabulary-shard points")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -220,6 +222,37 @@ def bench_workload(cid, args, torch, np):
     return inp, run, res
 
 
+SHARDS = 8  # vocabulary shards of the multi-GPU design; one shard's shape is timed here
+
+
+def bench_shard(cid, args, torch, np):
+    """tail_forward on one vocabulary shard's real shape: the workload's hidden
+    rows and params against shard 0 of its weight, W[:, :V / SHARDS] (what one
+    of 8 GPUs computes before the candidate exchange)."""
+    import decode_sampling_tail_amd as dst
+    inp, g, run = gpu_inputs(cid, torch, np)
+    Vs = inp.V // SHARDS
+    w = g["w_t"][:, :Vs].contiguous()
+    del g["w_t"]
+    f = dst.Forward(inp.gbs, inp.H, Vs, inp.k, inp.H_u, inp.eps, inp.zero_pad, deferred=True,
+                    emit_logits=False)
+    t_step = time_loop(torch, lambda: f(g["hidden"], g["gamma"], w, g["params"]), args.steps,
+                       args.warmup)
+    logits = torch.empty((inp.gbs, Vs), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dst.workspace_size(inp.gbs, inp.H, inp.H_u, Vs, inp.k, dst.EMIT_LOGITS),
+                     dtype=torch.uint8, device="cuda")
+    t_lm = time_loop(torch, lambda: dst.rmsnorm_lm_head(g["hidden"], g["gamma"], w, inp.H_u, inp.eps,
+                                                        inp.zero_pad, True, out=logits, ws=ws),
+                     args.steps, args.warmup)
+    lm_bytes = (inp.H_u * Vs * 2 + inp.gbs * inp.H_u * inp.hidden.dtype.itemsize + inp.H_u * 4 +
+                inp.gbs * Vs * 4 + inp.gbs * 4)
+    res = dict(gbs=inp.gbs, V_shard=Vs, ms_per_step=t_step * 1e3, tokens_per_s=inp.gbs / t_step,
+               rmsnorm_lm_head_us=t_lm * 1e6, lm_head_gbs=lm_bytes / t_lm / 1e9)
+    del g, w, f, logits, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(inp, run, budget_s=12.0):
     """The fp64 oracle, as it stands, on whole tail steps of the headline workload."""
     import numpy as np
@@ -273,6 +306,14 @@ def main():
         if cid == 1:
             head_inp, head_run = inp, run
 
+    shard = {}
+    if not args.no_sweep and not args.no_shard and not args.workload:
+        for label, cid in workloads():
+            log(f"shard point {label}: V / {SHARDS} columns")
+            shard[label] = bench_shard(cid, args, torch, np)
+            log(f"shard {label}: {shard[label]['ms_per_step'] * 1e3:.1f} us/step, "
+                f"lm_head {shard[label]['lm_head_gbs']:.0f} GB/s")
+
     if "gptoss_tail_gbs1" not in results:  # a profiling run of another workload
         print(json.dumps(dict(metric=METRIC, by_gbs=results)), flush=True)
         return
@@ -295,7 +336,8 @@ def main():
                ms_p10_p50_p90_evented=head["ms_p10_p50_p90_evented"],
                by_gbs={lbl: dict(r, lm_head_hbm_frac=r["lm_head_gbs"] / HBM_PEAK)
                        for lbl, r in results.items()},
-               source_hash=kernel_source_hash())
+               source_hash=kernel_source_hash(),
+               vocab_shard_points=shard or None)
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on the headline workload")
         out["cpu_baseline"] = cpu_baseline(head_inp, head_run)

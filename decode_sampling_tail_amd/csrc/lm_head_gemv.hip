@@ -29,6 +29,14 @@
 // r (scale) is finished in the epilogue.  In-chain: the whole row's r comes
 // first and y = (x * r) * gamma (scale = 1).
 //
+// Split K: a narrow vocabulary (one shard of a vocabulary-parallel layout)
+// has too few 512-column slabs to fill the chip, so the K lanes are also cut
+// into KC contiguous ranges, one per grid row (blockIdx.y); each workgroup
+// writes its unscaled partial sums (and, for the deferred fused RMSNorm, its
+// range's partial sum of squares) and reduce_kernel adds the KC partials in
+// range order, finishes r, scales, and writes the logits and group maxima.
+// KC depends only on V and K, so a row's logits do not depend on the batch.
+//
 // Page precision (parameters "deferred_rms" and "skip_nan_fold": one bf16
 // rounding of the GEMM input per element, bf16 products summed in fp32):
 // every activation is rounded to bf16 where it is formed (fused) or read
@@ -82,6 +90,10 @@ struct GemvArgs {
   float* r_out;            // fused only (may be NULL): per-row r
   uint32_t* gkey;
   int groups, b0;
+  int kc_n;      // K ranges (gridDim.y); > 1: partial sums go to part
+  int gbs;       // rows of the whole call (partial buffer stride)
+  float* part;   // [kc_n][gbs][V] partial sums (kc_n > 1)
+  double* pss;   // [kc_n][gbs] partial sums of squares (kc_n > 1, fused deferred)
 };
 
 template <int NB, int SRC, int W = kWaves, int U = kUnroll>
@@ -99,8 +111,11 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
   const bool act = col < a.V;
   const int K = a.K, V = a.V, pad_s = a.pad_s;
 
-  const int u0 = (wave * K) / W;
-  const int u1 = ((wave + 1) * K) / W;
+  // this workgroup's K range, cut among its waves
+  const int kc = blockIdx.y;
+  const int kb0 = int((long long)K * kc / a.kc_n), kb1 = int((long long)K * (kc + 1) / a.kc_n);
+  const int u0 = kb0 + ((kb1 - kb0) * wave) / W;
+  const int u1 = kb0 + ((kb1 - kb0) * (wave + 1)) / W;
   int h = pad_s ? u0 + int(fastdiv(uint32_t(u0), a.pdiv)) : u0;
   int gpos = pad_s ? h % pad_s : 0;
   const uint16_t* wcol = a.w + col;
@@ -192,7 +207,7 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
           const float yv = (s_y[b * K + u] * r) * a.gamma[hp];
           s_y[b * K + u] = a.page ? bf16_round(yv) : yv;
         }
-        if (tid == 0 && a.r_out) a.r_out[a.b0 + b] = r;
+        if (tid == 0 && kc == 0 && blockIdx.x == 0 && a.r_out) a.r_out[a.b0 + b] = r;
       }
       __syncthreads();
     }
@@ -268,7 +283,25 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
     __syncthreads();
   }
 
-  if (wave == 0) {
+  if (wave == 0 && a.kc_n > 1) {
+    // split K: the unscaled partial sums of this range (and, deferred fused,
+    // its partial sum of squares); reduce_kernel finishes them
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (act) {
+        float4* out = reinterpret_cast<float4*>(
+            a.part + (size_t(kc) * a.gbs + a.b0 + b) * V + col);
+        out[0] = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+        out[1] = make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
+      }
+      if (scale_at_end && lane == 0 && blockIdx.x == 0) {
+        double tot = 0.0;  // the wave partials in wave order
+#pragma unroll
+        for (int w = 0; w < W; ++w) tot += s_part[b][w];
+        a.pss[size_t(kc) * a.gbs + a.b0 + b] = tot;
+      }
+    }
+  } else if (wave == 0) {
     if (scale_at_end) {  // every wave's partial sum of squares is visible after the tree
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -303,6 +336,55 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
         if ((lane & 7) == 0 && g < a.groups) a.gkey[size_t(a.b0 + b) * a.groups + g] = m;
       }
     }
+  }
+}
+
+// Split-K finish: one wave per (512-column slab, row); lane l owns columns
+// 8 l .. 8 l + 7 of the slab.  Sums the kc_n partials in range order, then
+// scales by row_scale (given), by r from the kc_n partial sums of squares
+// (deferred fused RMSNorm; r also goes to r_out), or by 1.
+__global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ part,
+                                                    const double* __restrict__ pss, int kc_n,
+                                                    int gbs, int V, const float* __restrict__ row_scale,
+                                                    int H_u, float eps, float* __restrict__ r_out,
+                                                    float* __restrict__ logits,
+                                                    uint32_t* __restrict__ gkey, int groups) {
+  const int lane = threadIdx.x, b = blockIdx.y;
+  const int col = blockIdx.x * kSlab + lane * 8;
+  const bool act = col < V;
+  float scale = 1.0f;
+  if (pss) {
+    double tot = 0.0;
+    for (int kc = 0; kc < kc_n; ++kc) tot += pss[size_t(kc) * gbs + b];
+    scale = float(1.0 / sqrt(tot / double(H_u) + double(eps)));
+    if (lane == 0 && blockIdx.x == 0 && r_out) r_out[b] = scale;
+  } else if (row_scale) {
+    scale = row_scale[b];
+  }
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (act) {
+    for (int kc = 0; kc < kc_n; ++kc) {
+      const float4* p = reinterpret_cast<const float4*>(part + (size_t(kc) * gbs + b) * V + col);
+      const float4 x = p[0], y = p[1];
+      o[0] += x.x; o[1] += x.y; o[2] += x.z; o[3] += x.w;
+      o[4] += y.x; o[5] += y.y; o[6] += y.z; o[7] += y.w;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] *= scale;
+    float4* out = reinterpret_cast<float4*>(logits + size_t(b) * V + col);
+    out[0] = make_float4(o[0], o[1], o[2], o[3]);
+    out[1] = make_float4(o[4], o[5], o[6], o[7]);
+  }
+  if (gkey) {
+    uint32_t m = 0;
+    if (act) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) m = max(m, float_key(o[c]));
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    const int g = blockIdx.x * (kSlab / kFusedGroup) + lane / 8;
+    if ((lane & 7) == 0 && g < groups) gkey[size_t(b) * groups + g] = m;
   }
 }
 
@@ -342,16 +424,60 @@ hipError_t launch_pass(int nb, dim3 grid, hipStream_t st, const GemvArgs& a) {
 
 }  // namespace
 
+// K ranges for a V-column lm_head: one when the 512-column slabs fill the
+// chip's 256 CUs, else enough to make about 384 workgroups, each keeping at
+// least 256 K lanes (a design constant, so workspace sizes stay host-only).
+int gemv_ksplit(int V, int K) {
+  const int slabs = (V + kSlab - 1) / kSlab;
+  if (slabs >= 256) return 1;
+  int kc = (384 + slabs - 1) / slabs;
+  const int cap = K / 256 > 1 ? K / 256 : 1;
+  kc = kc < cap ? kc : cap;
+  return kc > 16 ? 16 : (kc < 1 ? 1 : kc);
+}
+
+size_t gemv_part_bytes(int gbs, int K, int V) {
+  const int kc = gemv_ksplit(V, K);
+  if (kc <= 1) return 0;
+  return align256(size_t(kc) * gbs * V * 4) + align256(size_t(kc) * gbs * 8);
+}
+
 bool gemv_fusable(int gbs, int K) {
   return gbs <= kGemvMaxBatch &&
          size_t(kWaves / 2) * gbs * kSlab * 4 + size_t(gbs) * K * 4 <= 96 * 1024;
 }
 
+hipError_t launch_part_reduce(const float* part, int kc_n, int gbs, int V, const float* row_scale,
+                              float* logits, uint32_t* gkey, hipStream_t st) {
+  dim3 grid((V + kSlab - 1) / kSlab, gbs);
+  hipLaunchKernelGGL(reduce_kernel, grid, dim3(64), 0, st, part, nullptr, kc_n, gbs, V, row_scale,
+                     0, 0.0f, nullptr, logits, gkey, (V + kFusedGroup - 1) / kFusedGroup);
+  return hipGetLastError();
+}
+
+namespace {
+// the split-K finish (no-op for one K range)
+hipError_t finish_ksplit(const GemvArgs& a, int gbs, const float* row_scale, bool deferred_fused,
+                         int H_u, float eps, float* r_out, hipStream_t st) {
+  if (a.kc_n <= 1) return hipSuccess;
+  dim3 grid((a.V + kSlab - 1) / kSlab, gbs);
+  hipLaunchKernelGGL(reduce_kernel, grid, dim3(64), 0, st, a.part,
+                     deferred_fused ? a.pss : nullptr, a.kc_n, gbs, a.V, row_scale, H_u, eps, r_out,
+                     a.logits, a.gkey, a.groups);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_lm_head_gemv(const float* y, int ldy, const uint16_t* w, const float* row_scale,
                                int gbs, int K, int pad_s, int V, bool page, float* logits,
-                               uint32_t* gkey, hipStream_t st) {
+                               uint32_t* gkey, void* part_ws, hipStream_t st) {
   GemvArgs a{};
   a.page = page ? 1 : 0;
+  a.gbs = gbs;
+  a.kc_n = gemv_ksplit(V, K);
+  a.part = static_cast<float*>(part_ws);
+  a.pss = reinterpret_cast<double*>(static_cast<char*>(part_ws) +
+                                    align256(size_t(a.kc_n) * gbs * V * 4));
   a.src = y;
   a.ldsrc = ldy;
   a.w = w;
@@ -363,22 +489,27 @@ hipError_t launch_lm_head_gemv(const float* y, int ldy, const uint16_t* w, const
   a.logits = logits;
   a.gkey = gkey;
   a.groups = (V + kFusedGroup - 1) / kFusedGroup;
-  dim3 grid((V + kSlab - 1) / kSlab);
+  dim3 grid((V + kSlab - 1) / kSlab, a.kc_n);
   for (int b0 = 0; b0 < gbs; b0 += kMaxNB) {
     a.b0 = b0;
     const int nb = gbs - b0 < kMaxNB ? gbs - b0 : kMaxNB;
     const hipError_t e = launch_pass<-1>(nb, grid, st, a);
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  return finish_ksplit(a, gbs, row_scale, false, 0, 0.0f, nullptr, st);
 }
 
 hipError_t launch_norm_gemv(const void* hidden, int dtype, const float* gamma, int gbs, int H,
                             int H_u, int K, int pad_s, float eps, bool deferred, bool page,
                             const uint16_t* w, int V, float* logits, float* r_out, uint32_t* gkey,
-                            hipStream_t st) {
+                            void* part_ws, hipStream_t st) {
   GemvArgs a{};
   a.page = page ? 1 : 0;
+  a.gbs = gbs;
+  a.kc_n = gemv_ksplit(V, K);
+  a.part = static_cast<float*>(part_ws);
+  a.pss = reinterpret_cast<double*>(static_cast<char*>(part_ws) +
+                                    align256(size_t(a.kc_n) * gbs * V * 4));
   a.src = hidden;
   a.ldsrc = H;
   a.gamma = gamma;
@@ -395,12 +526,15 @@ hipError_t launch_norm_gemv(const void* hidden, int dtype, const float* gamma, i
   a.gkey = gkey;
   a.groups = (V + kFusedGroup - 1) / kFusedGroup;
   a.b0 = 0;
-  dim3 grid((V + kSlab - 1) / kSlab);
+  dim3 grid((V + kSlab - 1) / kSlab, a.kc_n);
+  hipError_t e;
   switch (dtype) {
-    case 0: return launch_pass<0>(gbs, grid, st, a);
-    case 1: return launch_pass<1>(gbs, grid, st, a);
-    default: return launch_pass<2>(gbs, grid, st, a);
+    case 0: e = launch_pass<0>(gbs, grid, st, a); break;
+    case 1: e = launch_pass<1>(gbs, grid, st, a); break;
+    default: e = launch_pass<2>(gbs, grid, st, a); break;
   }
+  if (e != hipSuccess) return e;
+  return finish_ksplit(a, gbs, nullptr, deferred, H_u, eps, r_out, st);
 }
 
 }  // namespace tail

@@ -33,6 +33,13 @@
 //
 // Determinism: every output element is one fixed sequence of MFMAs (K-steps
 // in order, terms in order), the same for every column and every row.
+//
+// Split K (narrow vocabularies, e.g. one shard of a vocabulary-parallel
+// layout, whose 512-column tiles cannot fill the chip): grid row kc of KC
+// takes the K-steps [nks kc / KC, nks (kc + 1) / KC) and writes its unscaled
+// partial sums; a fixed-order reduction (shared with the weight-streaming
+// path) adds them, scales and writes the logits and group maxima.  KC depends
+// only on V and K.
 #include "tail_internal.h"
 
 namespace tail {
@@ -68,11 +75,12 @@ __device__ inline bf16x8 tr_operand(const unsigned char* s_w, int row, int col_b
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int VT, int WV, int WB, int NBT, int NT, int KT = 64, int MINB = 1>
+template <int VT, int WV, int WB, int NBT, int NT, int KT = 64, int MINB = 1, bool SPLIT = false>
 __global__ __launch_bounds__(WV * WB * 64, MINB) void mfma_kernel(
     const uint16_t* __restrict__ act, int rows_pad, int Kp, const uint16_t* __restrict__ w, int V,
     int H_u, int pad_s, FastDiv pdiv, const float* __restrict__ row_scale, int gbs, int b0,
-    float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups) {
+    float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups, int kc_n,
+    float* __restrict__ part) {
   using C = Cfg<VT, WV, WB, NBT, NT, KT>;
   __shared__ __align__(16) unsigned char s_w[KT * C::WROW];
   __shared__ __align__(16) unsigned char s_b[NT * C::BROWS * KT * 2];
@@ -83,6 +91,9 @@ __global__ __launch_bounds__(WV * WB * 64, MINB) void mfma_kernel(
   const int wv = wave % WV, wb = wave / WV;
   const int v0 = blockIdx.x * VT;
   const int nks = Kp / KT;  // Kp is a multiple of kKStep, which KT divides
+  // this workgroup's K-steps (all of them unless K is split)
+  const int ks0 = SPLIT ? int((long long)nks * blockIdx.y / kc_n) : 0;
+  const int ks1 = SPLIT ? int((long long)nks * (blockIdx.y + 1) / kc_n) : nks;
 
   for (int i = tid; i < C::BROWS * C::GPW; i += C::NTH) (&s_g[0][0])[i] = 0u;
 
@@ -142,12 +153,12 @@ __global__ __launch_bounds__(WV * WB * 64, MINB) void mfma_kernel(
   const int tr_row = 4 * kg + (s16 >> 2);
   const int tr_col = (wv * C::VW + 4 * (s16 & 3)) * 2;
 
-  load_w(0);
-  load_b(0);
-  for (int ks = 0; ks < nks; ++ks) {
+  load_w(ks0);
+  load_b(ks0);
+  for (int ks = ks0; ks < ks1; ++ks) {
     __syncthreads();
     store_lds();
-    if (ks + 1 < nks) {
+    if (ks + 1 < ks1) {
       load_w(ks + 1);
       load_b(ks + 1);
     }
@@ -174,6 +185,20 @@ __global__ __launch_bounds__(WV * WB * 64, MINB) void mfma_kernel(
   }
 
   // epilogue: lane holds v = 4 kg .. 4 kg + 3 of the tile for batch row s16
+  if constexpr (SPLIT) {  // split K: unscaled partial sums of this K range
+#pragma unroll
+    for (int bt = 0; bt < C::BTW; ++bt) {
+      const int b = b0 + wb * C::BW + bt * 16 + s16;
+#pragma unroll
+      for (int vt = 0; vt < C::VTW; ++vt) {
+        const int v = v0 + wv * C::VW + vt * 16 + 4 * kg;
+        if (b < gbs && v < V)
+          *reinterpret_cast<float4*>(part + (size_t(blockIdx.y) * gbs + b) * V + v) =
+              make_float4(acc[vt][bt][0], acc[vt][bt][1], acc[vt][bt][2], acc[vt][bt][3]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int bt = 0; bt < C::BTW; ++bt) {
     const int bl = wb * C::BW + bt * 16 + s16;
@@ -453,30 +478,40 @@ hipError_t launch_dma(const uint16_t* act, int rows_pad, int Kp, const uint16_t*
 template <int VT, int WV, int WB, int NBT, int NT, int KT = 64, int MINB = 1>
 hipError_t launch_cfg(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V, int H_u,
                       int pad_s, const float* row_scale, int gbs, int b0, float* logits,
-                      uint32_t* gkey, hipStream_t st) {
+                      uint32_t* gkey, int kc_n, float* part, hipStream_t st) {
   const FastDiv pdiv = make_fastdiv(pad_s > 1 ? uint32_t(pad_s - 1) : 1u);
   const int groups = (V + kFusedGroup - 1) / kFusedGroup;
-  dim3 grid((V + VT - 1) / VT), block(WV * WB * 64);
-  hipLaunchKernelGGL((mfma_kernel<VT, WV, WB, NBT, NT, KT, MINB>), grid, block, 0, st, act, rows_pad, Kp, w, V,
-                     H_u, pad_s, pdiv, row_scale, gbs, b0, logits, gkey, groups);
+  dim3 grid((V + VT - 1) / VT, kc_n), block(WV * WB * 64);
+  if (kc_n > 1)
+    hipLaunchKernelGGL((mfma_kernel<VT, WV, WB, NBT, NT, KT, MINB, true>), grid, block, 0, st, act,
+                       rows_pad, Kp, w, V, H_u, pad_s, pdiv, row_scale, gbs, b0, logits, gkey, groups,
+                       kc_n, part);
+  else
+    hipLaunchKernelGGL((mfma_kernel<VT, WV, WB, NBT, NT, KT, MINB, false>), grid, block, 0, st, act,
+                       rows_pad, Kp, w, V, H_u, pad_s, pdiv, row_scale, gbs, b0, logits, gkey, groups,
+                       kc_n, part);
   return hipGetLastError();
 }
 
 template <int NT>
 hipError_t launch_terms(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V,
                         int H_u, int pad_s, const float* row_scale, int gbs, float* logits,
-                        uint32_t* gkey, hipStream_t st) {
-  for (int b0 = 0; b0 < gbs; b0 += 256) {
-    const int rows = gbs - b0 < 256 ? gbs - b0 : 256;
+                        uint32_t* gkey, void* part_ws, hipStream_t st) {
+  const int kc_n = mfma_ksplit(V, Kp);
+  float* part = static_cast<float*>(part_ws);
+  // a split K runs every chunk on the per-tile kernel (128-row chunks)
+  const int chunk = kc_n > 1 ? 128 : 256;
+  for (int b0 = 0; b0 < gbs; b0 += chunk) {
+    const int rows = gbs - b0 < chunk ? gbs - b0 : chunk;
     const int nbt = (rows + 15) / 16;
     hipError_t e;
     if (nbt <= 8) {
       // 512-column tiles (393 workgroups for GPT-OSS) and 32-row K-steps;
       // up to 64 rows two workgroups share a CU, so all are resident at once
-      if (nbt <= 1) e = launch_cfg<512, 4, 1, 1, NT, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else if (nbt <= 2) e = launch_cfg<512, 4, 1, 2, NT, 32, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else if (nbt <= 4) e = launch_cfg<512, 4, 1, 4, NT, 32, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
-      else e = launch_cfg<512, 4, 2, 8, NT, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, st);
+      if (nbt <= 1) e = launch_cfg<512, 4, 1, 1, NT, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, kc_n, part, st);
+      else if (nbt <= 2) e = launch_cfg<512, 4, 1, 2, NT, 32, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, kc_n, part, st);
+      else if (nbt <= 4) e = launch_cfg<512, 4, 1, 4, NT, 32, 2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, kc_n, part, st);
+      else e = launch_cfg<512, 4, 2, 8, NT, 32>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, b0, logits, gkey, kc_n, part, st);
     } else {
       // persistent, direct-copy kernel; rows past the chunk are never stored.
       // One term leaves LDS for a fourth ring stage.
@@ -484,6 +519,7 @@ hipError_t launch_terms(const uint16_t* act, int rows_pad, int Kp, const uint16_
     }
     if (e != hipSuccess) return e;
   }
+  if (kc_n > 1) return launch_part_reduce(part, kc_n, gbs, V, row_scale, logits, gkey, st);
   return hipSuccess;
 }
 
@@ -491,13 +527,32 @@ hipError_t launch_terms(const uint16_t* act, int rows_pad, int Kp, const uint16_
 
 int mfma_terms(int, bool page) { return page ? 1 : 2; }
 
+// K ranges of the matrix-core lm_head: one when its 512-column tiles fill the
+// chip's 256 CUs, else enough for about 384 workgroups, each keeping at least
+// 8 K-steps of 32 (a design constant, so workspace sizes stay host-only).
+int mfma_ksplit(int V, int Kp) {
+  const int tiles = (V + 511) / 512;
+  if (tiles >= 256) return 1;
+  int kc = (384 + tiles - 1) / tiles;
+  const int cap = Kp / 256 > 1 ? Kp / 256 : 1;
+  kc = kc < cap ? kc : cap;
+  return kc > 16 ? 16 : (kc < 1 ? 1 : kc);
+}
+
+size_t mfma_part_bytes(int gbs, int Kp, int V) {
+  const int kc = mfma_ksplit(V, Kp);
+  return kc > 1 ? align256(size_t(kc) * gbs * V * 4) : 0;
+}
+
 hipError_t launch_lm_head_mfma(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,
                                int V, int H_u, int pad_s, const float* row_scale, int gbs,
-                               float* logits, uint32_t* gkey, hipStream_t st) {
+                               float* logits, uint32_t* gkey, void* part_ws, hipStream_t st) {
   if (nt == 2)
-    return launch_terms<2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, logits, gkey, st);
+    return launch_terms<2>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, logits, gkey,
+                           part_ws, st);
   if (nt == 1)
-    return launch_terms<1>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, logits, gkey, st);
+    return launch_terms<1>(act, rows_pad, Kp, w, V, H_u, pad_s, row_scale, gbs, logits, gkey,
+                           part_ws, st);
   return hipErrorInvalidValue;
 }
 

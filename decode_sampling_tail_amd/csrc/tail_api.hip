@@ -69,8 +69,16 @@ SplitGeom split_geom(int gbs, int H, int H_u, int pad_s, unsigned flags) {
 }
 
 struct FwdLayout {
-  size_t y, r, act, logits, gkey, total;
+  size_t y, r, act, part, logits, gkey, total;
 };
+
+// split-K partials of the lm_head path this batch takes (narrow vocabularies)
+size_t gemv_part(int gbs, int H, int H_u, int pad_s, int V) {
+  const int K = pad_s ? H_u : H;
+  if (gbs <= tail::kGemvMaxBatch) return tail::gemv_part_bytes(gbs, K, V);
+  const int Kp = (K + tail::kKStep - 1) / tail::kKStep * tail::kKStep;
+  return tail::mfma_part_bytes(gbs, Kp, V);
+}
 
 FwdLayout forward_layout(int gbs, int H, int H_u, int pad_s, int V, int k, unsigned flags) {
   tail::TopkGeom g;
@@ -83,6 +91,8 @@ FwdLayout forward_layout(int gbs, int H, int H_u, int pad_s, int V, int k, unsig
   off = align256(off + size_t(gbs) * 4);
   L.act = off;
   off = align256(off + split_geom(gbs, H, H_u, pad_s, flags).bytes);
+  L.part = off;
+  off = align256(off + gemv_part(gbs, H, H_u, pad_s, V));
   L.logits = off;
   if (!(flags & TAIL_EMIT_LOGITS)) off = align256(off + size_t(gbs) * V * 4);
   L.gkey = off;
@@ -108,25 +118,26 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 // y (gbs*H floats) and act (split_geom bytes) are workspace.
 hipError_t norm_lm_head(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t,
                         int gbs, int H, int H_u, int V, float eps, int ps, unsigned flags, float* y,
-                        float* r, uint16_t* act, float* logits, uint32_t* gkey, hipStream_t st) {
+                        float* r, uint16_t* act, void* part, float* logits, uint32_t* gkey,
+                        hipStream_t st) {
   const bool deferred = flags & TAIL_DEFERRED_RMS, page = flags & TAIL_PAGE_PRECISION;
   const SplitGeom sg = split_geom(gbs, H, H_u, ps, flags);
   if (tail::gemv_fusable(gbs, sg.K))
     return tail::launch_norm_gemv(hidden, dtype, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, page,
-                                  w_t, V, logits, r, gkey, st);
+                                  w_t, V, logits, r, gkey, part, st);
   hipError_t e;
   if (gbs <= tail::kGemvMaxBatch) {
     e = tail::launch_rmsnorm(hidden, dtype, gamma, gbs, H, H_u, ps, eps, deferred, page, y, r, st);
     if (e == hipSuccess)  // y is already rounded in the page mode
       e = tail::launch_lm_head_gemv(y, H, w_t, deferred ? r : nullptr, gbs, sg.K, ps, V, false,
-                                    logits, gkey, st);
+                                    logits, gkey, part, st);
     return e;
   }
   e = tail::launch_split(hidden, dtype, true, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, sg.nt,
                          sg.rows_pad, sg.Kp, act, r, st);
   if (e == hipSuccess)
     e = tail::launch_lm_head_mfma(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
-                                  deferred ? r : nullptr, gbs, logits, gkey, st);
+                                  deferred ? r : nullptr, gbs, logits, gkey, part, st);
   return e;
 }
 
@@ -151,7 +162,10 @@ TAIL_API size_t tail_workspace_size(int gbs, int H, int H_u, int V, int k, unsig
   const int ps = pad_stride(H, H_u, flags);
   size_t fwd = forward_layout(gbs, H, H_u, ps, V, k, flags).total;
   size_t tk = topk_ws_bytes(gbs, V, k);
-  size_t lm = align256(split_geom(gbs, H, H_u, ps, flags).bytes);
+  // tail_lm_head: the split-K partials, after the split activations on the
+  // matrix-core path
+  const size_t lm = align256(split_geom(gbs, H, H_u, ps, flags).bytes) +
+                    align256(gemv_part(gbs, H, H_u, ps, V));
   size_t m = fwd > tk ? fwd : tk;
   return m > lm ? m : lm;
 }
@@ -188,17 +202,21 @@ TAIL_API int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_
       (row_scale && !aligned(row_scale, 4)))
     return TAIL_ERR_INVALID_ARG;
   const SplitGeom sg = split_geom(gbs, H, H_u, ps, flags);
-  if (int s = check_ws(ws, ws_bytes, sg.bytes)) return s;
   hipStream_t st = (hipStream_t)stream;
-  if (gbs <= tail::kGemvMaxBatch)
+  if (gbs <= tail::kGemvMaxBatch) {
+    if (int s = check_ws(ws, ws_bytes, gemv_part(gbs, H, H_u, ps, V))) return s;
     return hip_status(tail::launch_lm_head_gemv(y, H, w_t, row_scale, gbs, sg.K, ps, V,
-                                                flags & TAIL_PAGE_PRECISION, logits, nullptr, st));
+                                                flags & TAIL_PAGE_PRECISION, logits, nullptr, ws,
+                                                st));
+  }
+  // matrix-core path: the split activations, then the split-K partials
+  if (int s = check_ws(ws, ws_bytes, align256(sg.bytes) + gemv_part(gbs, H, H_u, ps, V))) return s;
   uint16_t* act = (uint16_t*)ws;
   hipError_t e = tail::launch_split(y, TAIL_F32, false, nullptr, gbs, H, H_u, sg.K, ps, 0.0f, false,
                                     sg.nt, sg.rows_pad, sg.Kp, act, nullptr, st);
   if (e == hipSuccess)
     e = tail::launch_lm_head_mfma(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps, row_scale, gbs,
-                                  logits, nullptr, st);
+                                  logits, nullptr, (char*)ws + align256(sg.bytes), st);
   return hip_status(e);
 }
 
@@ -223,8 +241,8 @@ TAIL_API int tail_rmsnorm_lm_head(const void* hidden, int dtype, const float* ga
   char* base = (char*)ws;
   float* r = out_r ? out_r : (float*)(base + L.r);
   return hip_status(norm_lm_head(hidden, dtype, gamma, w_t, gbs, H, H_u, V, eps, ps, flags,
-                                 (float*)(base + L.y), r,
-                                 (uint16_t*)(base + L.act), logits, nullptr, (hipStream_t)stream));
+                                 (float*)(base + L.y), r, (uint16_t*)(base + L.act),
+                                 base + L.part, logits, nullptr, (hipStream_t)stream));
 }
 
 namespace {
@@ -309,7 +327,7 @@ TAIL_API int tail_forward(const void* hidden, int dtype, const float* gamma, con
   const bool fused_groups = g.gs == tail::kFusedGroup && !fold;
   uint32_t* gk_fused = fused_groups ? gk : nullptr;
   hipError_t e = norm_lm_head(hidden, dtype, gamma, w_t, gbs, H, H_u, V, eps, ps, flags, y, r, act,
-                              lg, gk_fused, st);
+                              base + L.part, lg, gk_fused, st);
   if (e == hipSuccess && !fused_groups) e = tail::launch_group_max(lg, gbs, V, g, fold, gk, st);
   if (e == hipSuccess)
     e = tail::launch_select(lg, gbs, V, k, g, gk, flags & TAIL_PAGE_PRECISION, fold, vals, idx,

@@ -96,10 +96,14 @@ hipError_t launch_rmsnorm(const void* hidden, int dtype, const float* gamma, int
 // Weight-streaming lm_head over K contraction lanes (pad lanes skipped when
 // pad_s > 0).  gkey (may be NULL): per row, the largest order-preserving key
 // of each group of kFusedGroup columns, [gbs, ceil(V / kFusedGroup)].  page:
-// the activations are rounded to bf16 before the contraction.
+// the activations are rounded to bf16 before the contraction.  part_ws:
+// gemv_part_bytes(gbs, K, V) bytes (256-byte aligned) for the split-K
+// partials when the vocabulary is too narrow to fill the chip.
+int gemv_ksplit(int V, int K);
+size_t gemv_part_bytes(int gbs, int K, int V);
 hipError_t launch_lm_head_gemv(const float* y, int ldy, const uint16_t* w, const float* row_scale,
                                int gbs, int K, int pad_s, int V, bool page, float* logits,
-                               uint32_t* gkey, hipStream_t st);
+                               uint32_t* gkey, void* part_ws, hipStream_t st);
 
 // The same with the RMSNorm fused into the prologue (hidden rows in their
 // storage dtype); r_out (may be NULL) receives the per-row rms scale.
@@ -107,7 +111,7 @@ bool gemv_fusable(int gbs, int K);
 hipError_t launch_norm_gemv(const void* hidden, int dtype, const float* gamma, int gbs, int H,
                             int H_u, int K, int pad_s, float eps, bool deferred, bool page,
                             const uint16_t* w, int V, float* logits, float* r_out, uint32_t* gkey,
-                            hipStream_t st);
+                            void* part_ws, hipStream_t st);
 
 // Batches above this size run the lm_head on the matrix cores.
 constexpr int kGemvMaxBatch = 4;
@@ -122,9 +126,18 @@ hipError_t launch_split(const void* src, int dtype, bool norm, const float* gamm
                         int H_u, int K, int pad_s, float eps, bool deferred, int nt, int rows_pad,
                         int Kp, uint16_t* act, float* r, hipStream_t st);
 
+// Matrix-core lm_head; part_ws: mfma_part_bytes(gbs, Kp, V) bytes (256-byte
+// aligned) for the split-K partials of a narrow vocabulary.
+int mfma_ksplit(int V, int Kp);
+size_t mfma_part_bytes(int gbs, int Kp, int V);
 hipError_t launch_lm_head_mfma(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,
                                int V, int H_u, int pad_s, const float* row_scale, int gbs,
-                               float* logits, uint32_t* gkey, hipStream_t st);
+                               float* logits, uint32_t* gkey, void* part_ws, hipStream_t st);
+
+// Split-K finish shared by the lm_head paths: logits[b, v] = row_scale[b] (or
+// 1) * sum over kc in order of part[kc][b][v]; gkey (may be NULL) as above.
+hipError_t launch_part_reduce(const float* part, int kc_n, int gbs, int V, const float* row_scale,
+                              float* logits, uint32_t* gkey, hipStream_t st);
 
 // fold: NaN counts as -inf (the page's stage-1 NaN fold)
 hipError_t launch_group_max(const float* logits, int gbs, int V, const TopkGeom& geom, bool fold,
