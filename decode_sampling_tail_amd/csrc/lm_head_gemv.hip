@@ -388,13 +388,15 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* __restrict__ pa
   }
 }
 
-// Dynamic LDS above 64 KB needs the kernel's limit raised once per process.
+// Dynamic LDS above 64 KB needs the kernel's limit raised, once per device.
 template <int NB, int SRC>
 hipError_t raise_lds_limit() {
-  static const hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemv_kernel<NB, SRC>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-  return e;
+  static std::once_flag once[kMaxDevices];
+  static hipError_t status[kMaxDevices];
+  return per_device(once, status, [](int) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<NB, SRC>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+  });
 }
 
 template <int SRC>

@@ -454,22 +454,22 @@ hipError_t launch_dma(const uint16_t* act, int rows_pad, int Kp, const uint16_t*
                       int pad_s, const float* row_scale, int gbs, int b0, float* logits,
                       uint32_t* gkey, hipStream_t st) {
   auto kern = dma_kernel<VT, WV, WB, NBT, NT, NS>;
-  static int per_cu = -1;
-  if (per_cu < 0) {
-    int n = 0;
+  // resident workgroups of this kernel on the current device (once per device)
+  static std::once_flag once[kMaxDevices];
+  static int slots_cache[kMaxDevices];
+  const int slots = per_device(once, slots_cache, [&](int dev) {
+    int n = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, WV * WB * 64, 0) != hipSuccess ||
         n < 1)
       n = 1;
-    per_cu = n;
-  }
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < 1)
-    cus = 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    return n * cus;
+  });
   const FastDiv pdiv = make_fastdiv(pad_s > 1 ? uint32_t(pad_s - 1) : 1u);
   const int groups = (V + kFusedGroup - 1) / kFusedGroup;
-  const int P = min(groups, cus * per_cu);
+  const int P = min(groups, slots);
   hipLaunchKernelGGL(kern, dim3(P), dim3(WV * WB * 64), 0, st, act, rows_pad, Kp, w, V, K, pad_s,
                      pdiv, row_scale, gbs, b0, logits, gkey, groups);
   return hipGetLastError();

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace tail {
 
 // ------------------------------------------------------------ small helpers
@@ -57,6 +59,18 @@ __device__ inline uint32_t bf16_rne_bits(uint32_t u) {
 }
 __device__ inline float bf16_round(float f) {
   return __uint_as_float(bf16_rne_bits(__float_as_uint(f)) << 16);
+}
+
+// Once-per-device host initialization: init(dev) runs the first time a
+// device (the current one) needs it, thread-safely; later calls return its
+// cached value.  T must be default-constructible.
+constexpr int kMaxDevices = 64;
+template <typename T, typename F>
+T per_device(std::once_flag (&once)[kMaxDevices], T (&value)[kMaxDevices], F&& init) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return init(dev);
+  std::call_once(once[dev], [&] { value[dev] = init(dev); });
+  return value[dev];
 }
 
 // Order-preserving key of a float: larger float <=> larger unsigned key.
