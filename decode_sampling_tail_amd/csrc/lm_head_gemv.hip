@@ -8,18 +8,21 @@
 // The weight (K * V * 2 bytes, 1.16 GB for GPT-OSS) is read exactly once;
 // that read is the roofline of the whole tail at small batch.
 //
-// Mapping: a workgroup of W waves (8 by default) owns a slab of 512 consecutive
+// Mapping: a workgroup of W waves (4 by default) owns a slab of 512 consecutive
 // vocabulary columns; lane l of every wave owns columns 8l..8l+7 of the slab,
 // read as one non-temporal 16-byte load per weight row (a wave reads 1 KB
 // of a row per load).  The W waves split the K contraction lanes into W
 // contiguous ranges and keep NB x 8 fp32 partial sums each; loads run one
 // batch of U rows ahead of the FMAs.  Partials are combined through LDS in a
-// fixed tree (step d adds wave w + d into wave w, d = W/2 .. 1; for W = 8:
-// ((p0+p4)+(p2+p6)) + ((p1+p5)+(p3+p7))), so a column's sum depends only on
+// fixed tree (step d adds wave w + d into wave w, d = W/2 .. 1; for W = 4:
+// (p0+p2) + (p1+p3)), so a column's sum depends only on
 // K and the shape, never on the column's position or on the other rows.
 //
-// Activations: SRC < 0 reads a given fp32 y [gbs, H] through the scalar
-// cache (row index wave-uniform), scale = row_scale (or 1).  SRC = hidden
+// Activations: SRC < 0 takes a given fp32 y [gbs, H], scale = row_scale (or
+// 1).  SRC = -2 copies each wave's K range of the NB rows into an LDS table
+// first (compacted over the K lanes, like the fused table below); SRC = -1,
+// for rows too wide for LDS, reads y in the loop (row index wave-uniform), at
+// the cost of NB x U extra loads per batch.  SRC = hidden
 // dtype (0 fp32, 1 fp16, 2 bf16) fuses the RMSNorm: the prologue widens the
 // NB hidden rows exactly, accumulates each row's sum of squares in fp64 in a
 // fixed order (per wave over its lanes, then the W wave partials in order),
@@ -53,6 +56,9 @@ constexpr int kMaxNB = 8;   // batch rows per pass
 // default shape: waves per workgroup and weight rows per load batch
 constexpr int kWaves = 4;
 constexpr int kUnroll = 6;
+// K lanes per thread in one prologue burst (times NB rows held in registers)
+template <int NB>
+constexpr int kPrologueBurst = NB <= 4 ? 16 : 8;
 
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -69,9 +75,19 @@ __device__ inline float load_hidden(const void* p, size_t i) {
   }
 }
 
-__device__ inline double wave_sum(double v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// butterfly sums over the 64 lanes of NB independent values at once: every
+// step exchanges all NB values before it waits, so the NB reductions share
+// one chain of six exchanges (each value's order is the plain butterfly's)
+template <int NB>
+__device__ inline void wave_sums(double (&v)[NB]) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    double o[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) o[b] = __shfl_xor(v[b], off, 64);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) v[b] += o[b];
+  }
 }
 
 struct GemvArgs {
@@ -101,7 +117,7 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
   constexpr int kThreads = W * 64;
   extern __shared__ __align__(16) unsigned char smem[];
   float4* s_red = reinterpret_cast<float4*>(smem);                         // [W/2][NB][kSlab/4]
-  float* s_y = reinterpret_cast<float*>(smem + (W / 2) * NB * kSlab * 4);  // [NB][K] (fused)
+  float* s_y = reinterpret_cast<float*>(smem + (W / 2) * NB * kSlab * 4);  // [NB][K] (fused, SRC = -2)
   __shared__ double s_part[NB][W];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -143,57 +159,86 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
     const size_t rowbase = size_t(a.b0) * a.ldsrc;
     if (a.deferred) {
       // each wave builds only its own slice [u0, u1) of the y table and its
-      // partial sum of squares: no workgroup barrier before the main loop
-      // loads go out in bursts of kBurst lanes per thread (one memory
-      // latency per burst rather than one per element)
-      constexpr int kBurst = 16;
+      // partial sums of squares: no workgroup barrier before the main loop.
+      // One burst carries kBurst lanes per thread of gamma and of all NB rows
+      // (one memory latency per burst rather than one per element or row);
+      // a row's sum still runs over its lanes in ascending burst order
+      constexpr int kBurst = kPrologueBurst<NB>;
+      double ss[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        double ss = 0.0;
-        for (int c0 = u0; c0 < u1; c0 += 64 * kBurst) {
-          float x[kBurst], g[kBurst];
+      for (int b = 0; b < NB; ++b) ss[b] = 0.0;
+      for (int c0 = u0; c0 < u1; c0 += 64 * kBurst) {
+        float x[NB][kBurst], g[kBurst];
 #pragma unroll
-          for (int i = 0; i < kBurst; ++i) {
-            const int u = c0 + lane + 64 * i;
-            x[i] = 0.0f;
-            g[i] = 0.0f;
-            if (u < u1) {
-              const int hp = pad_s ? u + int(fastdiv(uint32_t(u), a.pdiv)) : u;
-              x[i] = load_hidden<SRC>(a.src, rowbase + size_t(b) * a.ldsrc + hp);
-              g[i] = a.gamma[hp];
-            }
+        for (int i = 0; i < kBurst; ++i) {
+          const int u = c0 + lane + 64 * i;
+          g[i] = 0.0f;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) x[b][i] = 0.0f;
+          if (u < u1) {
+            const int hp = pad_s ? u + int(fastdiv(uint32_t(u), a.pdiv)) : u;
+            g[i] = a.gamma[hp];
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+              x[b][i] = load_hidden<SRC>(a.src, rowbase + size_t(b) * a.ldsrc + hp);
           }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int i = 0; i < kBurst; ++i) {
             const int u = c0 + lane + 64 * i;
-            ss = fma(double(x[i]), double(x[i]), ss);
+            ss[b] = fma(double(x[b][i]), double(x[b][i]), ss[b]);
             if (u < u1) {
-              const float yv = x[i] * g[i];
+              const float yv = x[b][i] * g[i];
               s_y[b * K + u] = a.page ? bf16_round(yv) : yv;
             }
           }
-        }
-        ss = wave_sum(ss);
-        if (lane == 0) s_part[b][wave] = ss;
+      }
+      wave_sums<NB>(ss);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (lane == 0) s_part[b][wave] = ss[b];
         scale[b] = 1.0f;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       scale_at_end = true;
     } else {
-      // in-chain: r is needed before the contraction, so the whole row first
+      // in-chain: r is needed before the contraction, so the whole rows
+      // first, in bursts over all NB rows (a thread's lanes tid, tid + 256,
+      // ... in ascending order)
+      constexpr int kBurst = kPrologueBurst<NB>;
+      double ss[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        double ss = 0.0;
-        for (int u = tid; u < K; u += kThreads) {
-          const int hp = pad_s ? u + int(fastdiv(uint32_t(u), a.pdiv)) : u;
-          const float x = load_hidden<SRC>(a.src, rowbase + size_t(b) * a.ldsrc + hp);
-          ss = fma(double(x), double(x), ss);
-          s_y[b * K + u] = x;
+      for (int b = 0; b < NB; ++b) ss[b] = 0.0;
+      for (int c0 = 0; c0 < K; c0 += kThreads * kBurst) {
+        float x[NB][kBurst];
+#pragma unroll
+        for (int i = 0; i < kBurst; ++i) {
+          const int u = c0 + tid + kThreads * i;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) x[b][i] = 0.0f;
+          if (u < K) {
+            const int hp = pad_s ? u + int(fastdiv(uint32_t(u), a.pdiv)) : u;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+              x[b][i] = load_hidden<SRC>(a.src, rowbase + size_t(b) * a.ldsrc + hp);
+          }
         }
-        ss = wave_sum(ss);
-        if (lane == 0) s_part[b][wave] = ss;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int i = 0; i < kBurst; ++i) {
+            const int u = c0 + tid + kThreads * i;
+            ss[b] = fma(double(x[b][i]), double(x[b][i]), ss[b]);
+            if (u < K) s_y[b * K + u] = x[b][i];
+          }
       }
+      wave_sums<NB>(ss);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (lane == 0) s_part[b][wave] = ss[b];
       __syncthreads();
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -212,6 +257,35 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
       __syncthreads();
     }
   } else {
+    if constexpr (SRC == -2) {
+      // the wave's own K range of all NB rows, in bursts as the deferred
+      // prologue above
+      constexpr int kBurst = kPrologueBurst<NB>;
+      const float* y0 = static_cast<const float*>(a.src) + size_t(a.b0) * a.ldsrc;
+      for (int c0 = u0; c0 < u1; c0 += 64 * kBurst) {
+        float x[NB][kBurst];
+#pragma unroll
+        for (int i = 0; i < kBurst; ++i) {
+          const int u = c0 + lane + 64 * i;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) x[b][i] = 0.0f;
+          if (u < u1) {
+            const int hp = pad_s ? u + int(fastdiv(uint32_t(u), a.pdiv)) : u;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) x[b][i] = y0[size_t(b) * a.ldsrc + hp];
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int i = 0; i < kBurst; ++i) {
+            const int u = c0 + lane + 64 * i;
+            if (u < u1) s_y[b * K + u] = a.page ? bf16_round(x[b][i]) : x[b][i];
+          }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) scale[b] = a.row_scale ? a.row_scale[a.b0 + b] : 1.0f;
   }
@@ -223,7 +297,7 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
     for (int c = 0; c < 8; ++c) acc[b][c] = 0.0f;
 
   const float* yg = static_cast<const float*>(a.src) + size_t(a.b0) * a.ldsrc;
-  const bool page_src = SRC < 0 && a.page;
+  const bool page_src = SRC == -1 && a.page;
   for (int u = u0; u < u1; u += U) {
     uint4 nx[U];
     int nh[U];
@@ -237,7 +311,7 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
       for (int j = 0; j < U; ++j) {
         yv[b][j] = 0.0f;
         if (u + j < u1) {
-          if constexpr (SRC >= 0) yv[b][j] = s_y[b * K + u + j];
+          if constexpr (SRC != -1) yv[b][j] = s_y[b * K + u + j];
           else yv[b][j] = page_src ? bf16_round(yg[size_t(b) * a.ldsrc + hh[j]])
                                    : yg[size_t(b) * a.ldsrc + hh[j]];
         }
@@ -401,7 +475,7 @@ hipError_t raise_lds_limit() {
 
 template <int SRC>
 hipError_t launch_pass(int nb, dim3 grid, hipStream_t st, const GemvArgs& a) {
-  const size_t lds = size_t(kWaves / 2) * nb * kSlab * 4 + (SRC >= 0 ? size_t(nb) * a.K * 4 : 0);
+  const size_t lds = size_t(kWaves / 2) * nb * kSlab * 4 + (SRC != -1 ? size_t(nb) * a.K * 4 : 0);
 #define TAIL_GEMV(NB)                                                                   \
   do {                                                                                  \
     if (lds > 64 * 1024) {                                                              \
@@ -426,6 +500,14 @@ hipError_t launch_pass(int nb, dim3 grid, hipStream_t st, const GemvArgs& a) {
 
 }  // namespace
 
+namespace {
+// the reduction buffer and an NB x K fp32 activation table within the raised
+// LDS limit
+bool gemv_table_fits(int nb, int K) {
+  return size_t(kWaves / 2) * nb * kSlab * 4 + size_t(nb) * K * 4 <= 96 * 1024;
+}
+}  // namespace
+
 // K ranges for a V-column lm_head: one when the 512-column slabs fill the
 // chip's 256 CUs, else enough to make about 384 workgroups, each keeping at
 // least 256 K lanes (a design constant, so workspace sizes stay host-only).
@@ -444,10 +526,7 @@ size_t gemv_part_bytes(int gbs, int K, int V) {
   return align256(size_t(kc) * gbs * V * 4) + align256(size_t(kc) * gbs * 8);
 }
 
-bool gemv_fusable(int gbs, int K) {
-  return gbs <= kGemvMaxBatch &&
-         size_t(kWaves / 2) * gbs * kSlab * 4 + size_t(gbs) * K * 4 <= 96 * 1024;
-}
+bool gemv_fusable(int gbs, int K) { return gbs <= kGemvMaxBatch && gemv_table_fits(gbs, K); }
 
 hipError_t launch_part_reduce(const float* part, int kc_n, int gbs, int V, const float* row_scale,
                               float* logits, uint32_t* gkey, hipStream_t st) {
@@ -495,7 +574,8 @@ hipError_t launch_lm_head_gemv(const float* y, int ldy, const uint16_t* w, const
   for (int b0 = 0; b0 < gbs; b0 += kMaxNB) {
     a.b0 = b0;
     const int nb = gbs - b0 < kMaxNB ? gbs - b0 : kMaxNB;
-    const hipError_t e = launch_pass<-1>(nb, grid, st, a);
+    const hipError_t e = gemv_table_fits(nb, K) ? launch_pass<-2>(nb, grid, st, a)
+                                                : launch_pass<-1>(nb, grid, st, a);
     if (e != hipSuccess) return e;
   }
   return finish_ksplit(a, gbs, row_scale, false, 0, 0.0f, nullptr, st);
