@@ -204,19 +204,21 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
   };
 
   if (Kp / 8 <= kOct * kThreads) {
-    // the whole row in one burst, kept in registers: one memory latency
+    // the whole row in one burst, kept in registers: one memory latency.
+    // Deferred: the terms do not depend on r, so they are stored first and r
+    // (a block reduction) is finished while the stores drain
     float x[kOct][8], g[kOct][8];
     load_octets(0, x, g);
-    float r = 1.0f;
+    if (!NORM || deferred) emit_octets(0, x, g, 1.0f);
     if constexpr (NORM) {
       double ss = 0.0;
 #pragma unroll
       for (int i = 0; i < kOct; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) ss = fma(double(x[i][j]), double(x[i][j]), ss);
-      r = finish_r(ss);
+      const float r = finish_r(ss);
+      if (!deferred) emit_octets(0, x, g, r);
     }
-    emit_octets(0, x, g, r);
     return;
   }
   // longer rows: the sum of squares first, then the split, burst by burst

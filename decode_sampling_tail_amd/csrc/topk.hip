@@ -12,7 +12,7 @@
 //     the maxima in power-of-two bins).  At least k groups have a maximum >=
 //     t0 and each maximum is an element, so every top-k member is >= t0, and
 //     only groups whose maximum is >= t0 can hold one.
-//  b. Those groups are scanned (loads batched four deep per thread) and every
+//  b. Those groups are scanned (loads batched five deep per thread) and every
 //     element >= t0 is appended to an LDS list as the composite key
 //     (value key << 32) | ~index: larger value first, lower index first.
 //  c. Lists longer than 2k are cut to the k-th largest value v* (radix select)
@@ -62,7 +62,8 @@ constexpr int kGPer = kMaxGroups / kSelThreads;   // group keys per thread in re
 // the final ranking keeps 2k composites and 2k value bits in the group list's space
 static_assert(kMaxGroups >= 6 * TAIL_K_MAX, "group list too small for the sorted copy");
 constexpr int kBatch = 4;                         // float4 loads in flight per thread
-constexpr int kScanBatch = 4;                     // the same in the candidate scan (step b)
+constexpr int kScanBatch = 5;                     // the same in the candidate scan (step b)
+static_assert(kScanBatch * 4 <= 32, "the scan's per-thread hit mask is 32 bits");
 
 __device__ inline uint32_t wave_max_u32(uint32_t v) {
   for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
@@ -303,7 +304,10 @@ __device__ inline void for_candidates(const SelShared& s, const float* row, int 
 
 // Step b: append every element with key >= t0 to the LDS list.  Each thread
 // issues kScanBatch float4 loads at once and checks them together (a bit
-// mask; batches of 2 to 8 measured within 0.2 us of each other), the wave
+// mask).  Five per thread cover up to 320 candidate groups of 64 in one pass
+// (k = 256 rows of GPT-OSS hold about 265): the scan then took 4.6-5.1 us
+// against 5.1-5.8 us with four (two passes) and 6.1-6.5 us with eight (one
+// pass, but every thread checks 32 mostly empty slots).  The wave
 // prefix-sums the counts with shuffles, and one LDS atomic per wave and batch
 // reserves the slots (none when the wave found nothing, the common case);
 // positions past kCap are counted but not stored.  Same elements, keys and
