@@ -63,16 +63,23 @@ constexpr int kPrologueBurst = NB <= 4 ? 16 : 8;
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// A hidden element's raw bits (the fp32 pattern, or the 16-bit pattern
+// zero-extended), widened by widen_bits once the whole burst is issued.  The
+// prologues load every slot of a burst unconditionally, slots past the range
+// from a clamped valid lane, and zero those slots where the values are used:
+// a load inside a branch that widened its value (or that the compiler
+// widened there) had to complete before the branch closed, one memory
+// latency per element.
 template <int DT>
-__device__ inline float load_hidden(const void* p, size_t i) {
-  if constexpr (DT == 0) {
-    return static_cast<const float*>(p)[i];
-  } else if constexpr (DT == 1) {
-    return __half2float(static_cast<const __half*>(p)[i]);
-  } else {
-    const uint32_t b = static_cast<const uint16_t*>(p)[i];
-    return __uint_as_float(b << 16);
-  }
+__device__ inline uint32_t load_bits(const void* p, size_t i) {
+  if constexpr (DT == 0) return __float_as_uint(static_cast<const float*>(p)[i]);
+  else return static_cast<const uint16_t*>(p)[i];
+}
+template <int DT>
+__device__ inline float widen_bits(uint32_t b) {
+  if constexpr (DT == 0) return __uint_as_float(b);
+  else if constexpr (DT == 1) return __half2float(__ushort_as_half(uint16_t(b)));
+  else return __uint_as_float(b << 16);
 }
 
 // butterfly sums over the 64 lanes of NB independent values at once: every
@@ -151,7 +158,14 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
       }
     }
   };
-  load_batch(u0, wv, hh);  // in flight while the prologue runs
+  // The first weight batch is in flight while the prologue runs.  Prologues
+  // that build the LDS table issue their own first loads before it: loads
+  // complete in issue order, so the table's arithmetic then waits only for
+  // its inputs (small and mostly L2-resident), not for the weight batch
+  // behind them
+  bool table_first = SRC == -2;
+  if constexpr (SRC >= 0) table_first = a.deferred != 0;
+  if (!table_first) load_batch(u0, wv, hh);
 
   float scale[NB];
   bool scale_at_end = false;  // deferred fused RMSNorm: r is finished in the epilogue
@@ -167,33 +181,40 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
       double ss[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) ss[b] = 0.0;
-      for (int c0 = u0; c0 < u1; c0 += 64 * kBurst) {
-        float x[NB][kBurst], g[kBurst];
+      uint32_t xb[NB][kBurst];
+      float g[kBurst];
+      auto burst_load = [&](int c0) {
 #pragma unroll
         for (int i = 0; i < kBurst; ++i) {
           const int u = c0 + lane + 64 * i;
-          g[i] = 0.0f;
+          const int uc = u < K ? u : K - 1;
+          const int hp = pad_s ? uc + int(fastdiv(uint32_t(uc), a.pdiv)) : uc;
+          g[i] = a.gamma[hp];
 #pragma unroll
-          for (int b = 0; b < NB; ++b) x[b][i] = 0.0f;
-          if (u < u1) {
-            const int hp = pad_s ? u + int(fastdiv(uint32_t(u), a.pdiv)) : u;
-            g[i] = a.gamma[hp];
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-              x[b][i] = load_hidden<SRC>(a.src, rowbase + size_t(b) * a.ldsrc + hp);
-          }
+          for (int b = 0; b < NB; ++b)
+            xb[b][i] = load_bits<SRC>(a.src, rowbase + size_t(b) * a.ldsrc + hp);
         }
+      };
+      auto burst_use = [&](int c0) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int i = 0; i < kBurst; ++i) {
             const int u = c0 + lane + 64 * i;
-            ss[b] = fma(double(x[b][i]), double(x[b][i]), ss[b]);
+            const float x = u < u1 ? widen_bits<SRC>(xb[b][i]) : 0.0f;
+            ss[b] = fma(double(x), double(x), ss[b]);
             if (u < u1) {
-              const float yv = x[b][i] * g[i];
+              const float yv = x * g[i];
               s_y[b * K + u] = a.page ? bf16_round(yv) : yv;
             }
           }
+      };
+      burst_load(u0);
+      load_batch(u0, wv, hh);
+      burst_use(u0);
+      for (int c0 = u0 + 64 * kBurst; c0 < u1; c0 += 64 * kBurst) {
+        burst_load(c0);
+        burst_use(c0);
       }
       wave_sums<NB>(ss);
 #pragma unroll
@@ -213,26 +234,24 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) ss[b] = 0.0;
       for (int c0 = 0; c0 < K; c0 += kThreads * kBurst) {
-        float x[NB][kBurst];
+        uint32_t xb[NB][kBurst];
 #pragma unroll
         for (int i = 0; i < kBurst; ++i) {
           const int u = c0 + tid + kThreads * i;
+          const int uc = u < K ? u : K - 1;
+          const int hp = pad_s ? uc + int(fastdiv(uint32_t(uc), a.pdiv)) : uc;
 #pragma unroll
-          for (int b = 0; b < NB; ++b) x[b][i] = 0.0f;
-          if (u < K) {
-            const int hp = pad_s ? u + int(fastdiv(uint32_t(u), a.pdiv)) : u;
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-              x[b][i] = load_hidden<SRC>(a.src, rowbase + size_t(b) * a.ldsrc + hp);
-          }
+          for (int b = 0; b < NB; ++b)
+            xb[b][i] = load_bits<SRC>(a.src, rowbase + size_t(b) * a.ldsrc + hp);
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int i = 0; i < kBurst; ++i) {
             const int u = c0 + tid + kThreads * i;
-            ss[b] = fma(double(x[b][i]), double(x[b][i]), ss[b]);
-            if (u < K) s_y[b * K + u] = x[b][i];
+            const float x = u < K ? widen_bits<SRC>(xb[b][i]) : 0.0f;
+            ss[b] = fma(double(x), double(x), ss[b]);
+            if (u < K) s_y[b * K + u] = x;
           }
       }
       wave_sums<NB>(ss);
@@ -262,19 +281,18 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
       // prologue above
       constexpr int kBurst = kPrologueBurst<NB>;
       const float* y0 = static_cast<const float*>(a.src) + size_t(a.b0) * a.ldsrc;
-      for (int c0 = u0; c0 < u1; c0 += 64 * kBurst) {
-        float x[NB][kBurst];
+      float x[NB][kBurst];
+      auto burst_load = [&](int c0) {
 #pragma unroll
         for (int i = 0; i < kBurst; ++i) {
           const int u = c0 + lane + 64 * i;
+          const int uc = u < K ? u : K - 1;
+          const int hp = pad_s ? uc + int(fastdiv(uint32_t(uc), a.pdiv)) : uc;
 #pragma unroll
-          for (int b = 0; b < NB; ++b) x[b][i] = 0.0f;
-          if (u < u1) {
-            const int hp = pad_s ? u + int(fastdiv(uint32_t(u), a.pdiv)) : u;
-#pragma unroll
-            for (int b = 0; b < NB; ++b) x[b][i] = y0[size_t(b) * a.ldsrc + hp];
-          }
+          for (int b = 0; b < NB; ++b) x[b][i] = y0[size_t(b) * a.ldsrc + hp];
         }
+      };
+      auto burst_use = [&](int c0) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -282,6 +300,13 @@ __global__ __launch_bounds__(W * 64) void gemv_kernel(GemvArgs a) {
             const int u = c0 + lane + 64 * i;
             if (u < u1) s_y[b * K + u] = a.page ? bf16_round(x[b][i]) : x[b][i];
           }
+      };
+      burst_load(u0);
+      load_batch(u0, wv, hh);
+      burst_use(u0);
+      for (int c0 = u0 + 64 * kBurst; c0 < u1; c0 += 64 * kBurst) {
+        burst_load(c0);
+        burst_use(c0);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

@@ -22,16 +22,22 @@ constexpr int kThreads = 256;
 constexpr int kPer = 16;  // lanes per thread per burst
 constexpr int kBurst = kThreads * kPer;
 
+// A hidden element's raw bits (the fp32 pattern, or the 16-bit pattern
+// zero-extended) and their widening.  Bursts load every slot
+// unconditionally (slots past the row from a clamped valid index) and zero
+// the out-of-range slots after widening: a load inside a branch that widened
+// its value (or that the compiler widened there) had to complete before the
+// branch closed, one memory latency per element.
 template <int DT>
-__device__ inline float load_hidden(const void* p, size_t i) {
-  if constexpr (DT == 0) {
-    return static_cast<const float*>(p)[i];
-  } else if constexpr (DT == 1) {
-    return __half2float(static_cast<const __half*>(p)[i]);
-  } else {
-    uint32_t b = static_cast<const uint16_t*>(p)[i];
-    return __uint_as_float(b << 16);
-  }
+__device__ inline uint32_t load_bits(const void* p, size_t i) {
+  if constexpr (DT == 0) return __float_as_uint(static_cast<const float*>(p)[i]);
+  else return static_cast<const uint16_t*>(p)[i];
+}
+template <int DT>
+__device__ inline float widen_bits(uint32_t b) {
+  if constexpr (DT == 0) return __uint_as_float(b);
+  else if constexpr (DT == 1) return __half2float(__ushort_as_half(uint16_t(b)));
+  else return __uint_as_float(b << 16);
 }
 
 __device__ inline double wave_sum(double v) {
@@ -44,10 +50,16 @@ __device__ inline bool is_pad(int h, int pad_s) { return pad_s && (h % pad_s == 
 template <int DT>
 __device__ inline void load_burst(const void* hidden, size_t base, int h0, int H, int pad_s, int tid,
                                   float (&x)[kPer]) {
+  uint32_t xb[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int h = h0 + tid + i * kThreads;
-    x[i] = (h < H && !is_pad(h, pad_s)) ? load_hidden<DT>(hidden, base + h) : 0.0f;
+    xb[i] = load_bits<DT>(hidden, base + (h < H ? h : H - 1));
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int h = h0 + tid + i * kThreads;
+    x[i] = (h < H && !is_pad(h, pad_s)) ? widen_bits<DT>(xb[i]) : 0.0f;
   }
 }
 
@@ -145,19 +157,26 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
   constexpr int kOct = kPer / 8;  // octets per thread per burst
   // loads the lanes of octets o0 + tid + i * kThreads (zero past K)
   auto load_octets = [&](int o0, float (&x)[kOct][8], float (&g)[kOct][8]) {
+    uint32_t xb[kOct][8];
 #pragma unroll
     for (int i = 0; i < kOct; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int o = o0 + tid + i * kThreads;
         const int u = 32 * (o / 4) + 4 * (o % 4) + (j & 3) + 16 * (j >> 2);
-        x[i][j] = 0.0f;
+        const int uc = u < K ? u : K - 1;
+        const int h = pad_s ? uc + int(fastdiv(uint32_t(uc), pdiv)) : uc;
+        xb[i][j] = load_bits<DT>(src, base + h);
         g[i][j] = 1.0f;
-        if (u < K) {
-          const int h = pad_s ? u + int(fastdiv(uint32_t(u), pdiv)) : u;
-          x[i][j] = load_hidden<DT>(src, base + h);
-          if constexpr (NORM) g[i][j] = gamma[h];
-        }
+        if constexpr (NORM) g[i][j] = gamma[h];
+      }
+#pragma unroll
+    for (int i = 0; i < kOct; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int o = o0 + tid + i * kThreads;
+        const int u = 32 * (o / 4) + 4 * (o % 4) + (j & 3) + 16 * (j >> 2);
+        x[i][j] = u < K ? widen_bits<DT>(xb[i][j]) : 0.0f;
       }
   };
   // splits and stores the loaded octets
