@@ -398,16 +398,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // of the group maxima over [lo, hi] in power-of-two bins: the bin where the
   // count from the top first reaches k starts at t0, so at least k group
   // maxima (hence k elements) are >= t0.
+  // every slot is loaded (past the row's groups from its last group) before
+  // any is used: a load inside the bounds branch with its use folded in
+  // waited for each key in turn
   uint32_t gk[kGPer];
   uint32_t lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
   for (int j = 0; j < kGPer; ++j) {
     const int g = tid + j * kSelThreads;
-    gk[j] = g < groups ? gkey[size_t(row_id) * groups + g] : 0u;
-    if (g < groups) {
+    gk[j] = gkey[size_t(row_id) * groups + (g < groups ? g : groups - 1)];
+  }
+#pragma unroll
+  for (int j = 0; j < kGPer; ++j) {
+    if (tid + j * kSelThreads < groups) {
       if constexpr (MIRROR) gk[j] = mirror_key(gk[j]);
       lo = min(lo, gk[j]);
       hi = max(hi, gk[j]);
+    } else {
+      gk[j] = 0u;
     }
   }
   lo = wave_min_u32(lo);
