@@ -65,8 +65,38 @@ constexpr int kBatch = 4;                         // float4 loads in flight per 
 constexpr int kScanBatch = 5;                     // the same in the candidate scan (step b)
 static_assert(kScanBatch * 4 <= 32, "the scan's per-thread hit mask is 32 bits");
 
+// Wave-wide integer reductions and prefix sums through lane moves inside the
+// register file (DPP): quad permutations and row mirrors combine the 16 lanes
+// of a row, row shifts build a row's prefix, and the row broadcasts of lanes
+// 15 and 31 carry it across rows.  Integer results do not depend on the
+// order, and each step costs a few cycles where an LDS-routed shuffle costs
+// a round trip.  Every lane of the wave must be active.  A lane that
+// receives nothing from a move keeps `old`.
+template <int CTRL, int ROWS = 0xf, int BANKS = 0xf>
+__device__ inline uint32_t dpp_mov(uint32_t old, uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(v), CTRL, ROWS, BANKS, false));
+}
+template <typename Op>
+__device__ inline uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp_mov<0xb1>(v, v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_mov<0x4e>(v, v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_mov<0x141>(v, v));  // row_half_mirror
+  v = op(v, dpp_mov<0x140>(v, v));  // row_mirror: every lane holds its row's result
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
 __device__ inline uint32_t wave_max_u32(uint32_t v) {
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+// inclusive prefix sum in lane order
+__device__ inline uint32_t wave_incl_sum_u32(uint32_t v) {
+  v += dpp_mov<0x111>(0u, v);        // row_shr:1
+  v += dpp_mov<0x112>(0u, v);        // row_shr:2
+  v += dpp_mov<0x114>(0u, v);        // row_shr:4
+  v += dpp_mov<0x118>(0u, v);        // row_shr:8: prefix within each row
+  v += dpp_mov<0x142, 0xa>(0u, v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_mov<0x143, 0xc>(0u, v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
@@ -118,12 +148,10 @@ __device__ inline uint64_t composite(uint32_t key, int e) {
 }
 
 __device__ inline uint32_t wave_min_u32(uint32_t v) {
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off, 64));
-  return v;
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 __device__ inline uint32_t wave_sum_u32(uint32_t v) {
-  for (int off = 32; off >= 1; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, 64);
-  return v;
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
 // Block-wide radix select: the k-th largest (k >= 1) 32-bit key among those
@@ -187,11 +215,7 @@ __device__ uint32_t radix_kth(SelShared& s, int tid, uint32_t k, Visit&& visit, 
         c[j] = s.hist[255 - 4 * tid - j];
         loc += c[j];
       }
-      uint32_t incl = loc;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = (uint32_t)__shfl_up((int)incl, off, 64);
-        if (tid >= off) incl += t;
-      }
+      const uint32_t incl = wave_incl_sum_u32(loc);
       uint32_t run = incl - loc;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -223,7 +247,7 @@ __device__ inline void wave_append(SelShared& s, bool pred, uint32_t key, int e,
   if (mask == 0) return;
   uint32_t base = 0;
   if (lane == 0) base = atomicAdd(&s.cnt, (uint32_t)__popcll(mask));
-  base = (uint32_t)__shfl((int)base, 0, 64);
+  base = __builtin_amdgcn_readlane(base, 0);
   if (pred) {
     const uint32_t pos = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
     if (pos < kCap) {
@@ -356,15 +380,11 @@ __device__ inline void scan_candidates(SelShared& s, const float* row, int V, in
     }
     if (__ballot(mask != 0) == 0) continue;  // nothing in the whole wave
     const uint32_t cnt = __popc(mask);  // kScanBatch * 4 <= 32 bits
-    uint32_t incl = cnt;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t t = (uint32_t)__shfl_up((int)incl, off, 64);
-      if (lane >= off) incl += t;
-    }
-    const uint32_t wtot = (uint32_t)__shfl((int)incl, 63, 64);
+    const uint32_t incl = wave_incl_sum_u32(cnt);
+    const uint32_t wtot = __builtin_amdgcn_readlane(incl, 63);
     uint32_t base = 0;
     if (lane == 0) base = atomicAdd(&s.cnt, wtot);
-    base = (uint32_t)__shfl((int)base, 0, 64);
+    base = __builtin_amdgcn_readlane(base, 0);
     uint32_t pos = base + incl - cnt;
 #pragma unroll
     for (int j = 0; j < kScanBatch * 4; ++j) {
@@ -447,11 +467,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       c[j] = s.hist[255 - 4 * tid - j];
       loc += c[j];
     }
-    uint32_t incl = loc;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t t = (uint32_t)__shfl_up((int)incl, off, 64);
-      if (tid >= off) incl += t;
-    }
+    const uint32_t incl = wave_incl_sum_u32(loc);
     uint32_t run = incl - loc;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -470,7 +486,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (m) {
       uint32_t base = 0;
       if (lane == 0) base = atomicAdd(&s.nact, (uint32_t)__popcll(m));
-      base = (uint32_t)__shfl((int)base, 0, 64);
+      base = __builtin_amdgcn_readlane(base, 0);
       if (a) s.act[base + __popcll(m & ((1ull << lane) - 1ull))] = uint32_t(tid + j * kSelThreads);
     }
   }
@@ -552,7 +568,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       if (m) {
         uint32_t base = 0;
         if (lane == 0) base = atomicAdd(&s.cnt, (uint32_t)__popcll(m));
-        base = (uint32_t)__shfl((int)base, 0, 64);
+        base = __builtin_amdgcn_readlane(base, 0);
         if (keep) {
           const uint32_t pos = base + __popcll(m & ((1ull << lane) - 1ull));
           s.c[pos] = mine[j];
@@ -604,11 +620,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         c[j] = s.hist[4 * tid + j];
         loc += c[j];
       }
-      uint32_t incl = loc;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = (uint32_t)__shfl_up((int)incl, off, 64);
-        if (tid >= off) incl += t;
-      }
+      const uint32_t incl = wave_incl_sum_u32(loc);
       uint32_t run = incl - loc;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
