@@ -131,6 +131,47 @@ __global__ __launch_bounds__(kGmThreads) void group_max_kernel(const float* __re
   if (lane == 0) gkey[size_t(row) * groups + g] = m;
 }
 
+// Group maxima for groups of 4 to 256 columns (q = gs / 4 float4 each):
+// every lane of a wave loads float4s, SPAN of them in flight, and the q lanes
+// of each group combine their keys in place (quad permutations and row
+// mirrors up to 16 lanes, shuffles across rows for 32 and 64), so every load
+// instruction moves 1 KB whatever the group size; the group's first lane
+// writes its key.  (group_max_kernel, one wave per group, serves the other
+// sizes.)  One row (small batches) takes one load per lane, so that more
+// waves share its latency; four from 8 rows up.
+template <int LQ, int SPAN>
+__global__ __launch_bounds__(kGmThreads) void span_max_kernel(const float* __restrict__ logits,
+                                                              int V, int groups, int fold,
+                                                              uint32_t* __restrict__ gkey) {
+  constexpr int Q = 1 << LQ;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.y;
+  const int nf = V >> 2;  // float4 per row (V is a multiple of 8)
+  const float4* p = reinterpret_cast<const float4*>(logits + size_t(row) * V);
+  const int f0 = (blockIdx.x * (kGmThreads / 64) + wave) * (64 * SPAN) + lane;
+  float4 v[SPAN];
+#pragma unroll
+  for (int s = 0; s < SPAN; ++s) {
+    const int f = f0 + 64 * s;
+    v[s] = p[f < nf ? f : nf - 1];  // past the row: a valid element, not used
+  }
+#pragma unroll
+  for (int s = 0; s < SPAN; ++s) {
+    const int f = f0 + 64 * s;
+    uint32_t m = 0u;
+    if (f < nf)
+      m = max(max(fold_key(v[s].x, fold), fold_key(v[s].y, fold)),
+              max(fold_key(v[s].z, fold), fold_key(v[s].w, fold)));
+    if constexpr (Q >= 2) m = max(m, dpp_mov<0xb1>(m, m));   // quad_perm [1,0,3,2]
+    if constexpr (Q >= 4) m = max(m, dpp_mov<0x4e>(m, m));   // quad_perm [2,3,0,1]
+    if constexpr (Q >= 8) m = max(m, dpp_mov<0x141>(m, m));  // row_half_mirror
+    if constexpr (Q >= 16) m = max(m, dpp_mov<0x140>(m, m)); // row_mirror
+    if constexpr (Q >= 32) m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+    if constexpr (Q >= 64) m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+    if ((lane & (Q - 1)) == 0 && f < nf) gkey[size_t(row) * groups + (f >> LQ)] = m;
+  }
+}
+
 struct SelShared {
   uint32_t act[kMaxGroups];  // candidate groups of the row
   uint64_t c[kCap];          // candidate composite keys
@@ -673,6 +714,32 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
 hipError_t launch_group_max(const float* logits, int gbs, int V, const TopkGeom& geom, bool fold,
                             uint32_t* gkey, hipStream_t st) {
+  const int gs = geom.gs;
+  if (gs >= 4 && gs <= 256) {
+    const int span = gbs < 8 ? 1 : 4;
+    const int per_block = 64 * span * (kGmThreads / 64);  // float4 per workgroup
+    dim3 grid((V / 4 + per_block - 1) / per_block, gbs);
+#define TAIL_SPAN_MAX(LQ)                                                                       \
+  do {                                                                                          \
+    if (span == 1)                                                                              \
+      hipLaunchKernelGGL((span_max_kernel<LQ, 1>), grid, dim3(kGmThreads), 0, st, logits, V,    \
+                         geom.groups, int(fold), gkey);                                         \
+    else                                                                                        \
+      hipLaunchKernelGGL((span_max_kernel<LQ, 4>), grid, dim3(kGmThreads), 0, st, logits, V,    \
+                         geom.groups, int(fold), gkey);                                         \
+  } while (0)
+    switch (gs) {
+      case 4: TAIL_SPAN_MAX(0); break;
+      case 8: TAIL_SPAN_MAX(1); break;
+      case 16: TAIL_SPAN_MAX(2); break;
+      case 32: TAIL_SPAN_MAX(3); break;
+      case 64: TAIL_SPAN_MAX(4); break;
+      case 128: TAIL_SPAN_MAX(5); break;
+      default: TAIL_SPAN_MAX(6); break;
+    }
+#undef TAIL_SPAN_MAX
+    return hipGetLastError();
+  }
   const int gpb = kGmThreads / 64;
   dim3 g1((geom.groups + gpb - 1) / gpb, gbs);
   hipLaunchKernelGGL(group_max_kernel, g1, dim3(kGmThreads), 0, st, logits, V, geom.gs, geom.groups,
