@@ -75,10 +75,11 @@ def test_max_hidden(gbs, zp):
     run_case(gbs, H, H_u, 1032, 32, zp, 2 + gbs, synth.DT_F16)
 
 
-@pytest.mark.parametrize("V,k", [(524352, 256), (1048576, 1024)])
+@pytest.mark.parametrize("V,k", [(524352, 256), (1048576, 1024), (1310720, 256), (2621440, 64)])
 def test_wide_vocab_topk(V, k):
-    """More than 8192 groups of 64 columns: the groups grow to 128, and the
-    group maxima come from a separate pass (tail_topk alone)."""
+    """More than 8192 groups of 64 columns: the groups grow to 128, 256 or 512
+    columns, and the group maxima come from a separate pass (tail_topk alone):
+    in-place lane combining up to 256 columns, one wave per group above."""
     rng = np.random.default_rng(V)
     L = rng.standard_normal((2, V)).astype(np.float32)
     L[1, rng.integers(0, V, 3000)] = 4.0  # exact ties above the k-th value
