@@ -49,12 +49,20 @@ __device__ inline int32_t sample_row_wave(VP vals, IP ix, int k, float top_k, fl
 #pragma unroll
   for (int j = 0; j < P; ++j) S[j] += excl;
 
+  // a lane's value read by every lane (the source lane is the same on all of
+  // them: v_readlane, no LDS round trip)
+  auto read_lane = [](double v, int src) {
+    const uint64_t b = __double_as_longlong(v);
+    const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(b), src);
+    const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(b >> 32), src);
+    return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+  };
   auto S_at = [&](int i) {  // S_i broadcast from its owner lane
     double mine = 0.0;
 #pragma unroll
     for (int j = 0; j < P; ++j)
       if (j == i % P) mine = S[j];
-    return __shfl(mine, i / P, 64);
+    return read_lane(mine, __builtin_amdgcn_readfirstlane(i / P));
   };
 
   // first candidate (in lane-major order) meeting a cut: the first lane with a
@@ -67,7 +75,8 @@ __device__ inline int32_t sample_row_wave(VP vals, IP ix, int k, float top_k, fl
       if (i < lim && (inclusive ? S[j] >= thr : S[j] > thr)) mine = i;
     }
     const uint64_t hits = __ballot(mine != INT_MAX);
-    return hits ? __shfl(mine, __ffsll((unsigned long long)hits) - 1, 64) : INT_MAX;
+    return hits ? int(__builtin_amdgcn_readlane(uint32_t(mine), __ffsll((unsigned long long)hits) - 1))
+                : INT_MAX;
   };
 
   const int first_p = first_hit(kk, double(top_p) * S_at(kk - 1), true);
