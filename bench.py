@@ -305,7 +305,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the tail runs with the whole vocabulary on one device)", file=sys.stderr)
         sys.exit(2)
     import numpy as np

@@ -149,7 +149,7 @@ TAIL_API const char* tail_status_string(int status) {
   switch (status) {
     case TAIL_OK: return "ok";
     case TAIL_ERR_INVALID_ARG: return "invalid argument";
-    case TAIL_ERR_UNSUPPORTED: return "unsupported by this build";
+    case TAIL_ERR_UNSUPPORTED: return "unsupported by this library";
     case TAIL_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case TAIL_ERR_HIP: return "HIP launch error";
     default: return "unknown status";

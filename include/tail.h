@@ -38,7 +38,7 @@ extern "C" {
 /* status codes */
 #define TAIL_OK 0
 #define TAIL_ERR_INVALID_ARG 1 /* a size, pointer, flag or dtype is out of its domain */
-#define TAIL_ERR_UNSUPPORTED 2 /* valid, but outside what this build implements */
+#define TAIL_ERR_UNSUPPORTED 2 /* valid, but outside what the library implements */
 #define TAIL_ERR_WORKSPACE 3   /* workspace missing, misaligned or too small */
 #define TAIL_ERR_HIP 4         /* the HIP runtime rejected a launch */
 
@@ -57,7 +57,7 @@ extern "C" {
  * tail_rmsnorm, tail_lm_head and tail_rmsnorm_lm_head take the first four,
  * tail_forward all five, tail_topk_ex TAIL_PAGE_PRECISION and TAIL_NAN_FOLD. */
 
-/* limits of this build */
+/* limits of the library */
 #define TAIL_K_MAX 1024      /* largest k ("k": 256 in production) */
 #define TAIL_GBS_MAX 4096    /* largest batch */
 #define TAIL_H_MAX 65536     /* largest hidden width */
