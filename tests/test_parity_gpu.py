@@ -144,6 +144,29 @@ def test_lm_head_duplicate_columns_and_batch_invariance(big, H):
         assert np.array_equal(Ls, Lb[b0:b0 + small])
 
 
+@pytest.mark.parametrize("page", [False, True])
+def test_lm_head_persistent_uneven_groups(page):
+    """Above 128 rows, on a vocabulary whose 64-column groups do not divide
+    over the persistent kernel's workgroups (some of them take a partial
+    extra sub-tile), the logits meet the parity bar and columns duplicated
+    between the whole sub-tiles and the partial ones give bitwise equal
+    logits (every element takes its full K in order)."""
+    rng = np.random.default_rng(11 + page)
+    gbs, H, V = 160, 256, 196928  # 3077 groups over 256 workgroups
+    w = bf16_bits(rng.standard_normal((H, V)) * 0.05)
+    cut = 3072 * 64
+    src = rng.choice(cut, 48, replace=False)
+    dup = cut + rng.choice(V - cut, 48, replace=False)
+    w[:, dup] = w[:, src]
+    y = rng.standard_normal((gbs, H)).astype(np.float32)
+    L = np_(dst.lm_head(torch.from_numpy(y).cuda(), gpu_bf16(w), page=page))
+    assert np.array_equal(L[:, src], L[:, dup])
+    yr = oracle.bf16_round(y) if page else y.astype(np.float64)
+    ref = oracle.logits(np.asarray(yr, np.float64), w, np.zeros(H, bool))
+    fails, rel, mx = check_logits(L, ref)
+    assert not fails, fails
+
+
 # ------------------------------------------------------------------- top-k
 def _topk_case(kind, gbs, V, rng):
     if kind == "normal":
