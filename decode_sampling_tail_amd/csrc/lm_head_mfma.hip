@@ -256,6 +256,19 @@ __global__ __launch_bounds__(WV * WB * 64, MINB) void mfma_kernel(
 // Rows past K and columns past V are fetched from clamped (valid) addresses:
 // a clamped weight row meets zero activations, and clamped columns or row
 // tiles only reach outputs that are never stored.
+//
+// Leftover items (two terms): when the groups do not divide evenly and the
+// one extra group of some workgroups would cost them a whole extra pass (a
+// step costs about the same however few columns it carries), the contiguous
+// ranges cover only gmain = P * floor(G / P) groups and the columns past
+// them are cut into VT-column regions, each dealt as WB items of one region
+// x one row group (the BTW row tiles of the waves with that wb).  An item
+// step carries two 32-row K blocks in the same stage bytes and copy count as
+// a whole-pass step: block 0's weights in the weight slot, block 1's in the
+// first half of the fragment slots, and the row group's fragments of both
+// blocks in the second half.  An item so takes half a pass's steps; only its
+// row group's waves run MFMAs and write outputs, and every element still
+// takes its full K in order, so the logits are the same bytes.
 template <int VT, int WV, int WB, int NBT, int NT, int NS>
 struct DCfg {
   static constexpr int NW = WV * WB, NTH = NW * 64;
@@ -265,6 +278,9 @@ struct DCfg {
   static constexpr int BINS = NT * NBT, NINS = WINS + BINS;        // copies per step
   static constexpr int WAIT = NINS / NW;                           // fewest copies of any wave
   static constexpr int STAGE = WBYTES + BINS * 1024;
+  // leftover items need two terms and a stage that holds two weight blocks
+  // plus one row group's fragments of both
+  static constexpr bool ITEMS = NT == 2 && 2 * WINS + 2 * NT * BTW == NINS;
   static_assert(VTW * 16 * WV == VT && VTW % 4 == 0 && BTW * WB == NBT && WPITCH <= 1024 &&
                     VT >= 128 && (VT & (VT - 1)) == 0 && WAIT >= 1 && NS >= 2 &&
                     WAIT * (NS - 2) < 64 && NS * STAGE <= 160 * 1024,
@@ -295,7 +311,7 @@ template <int VT, int WV, int WB, int NBT, int NT, int NS>
 __global__ __launch_bounds__(WV * WB * 64) void dma_kernel(
     const uint16_t* __restrict__ act, int rows_pad, int Kp, const uint16_t* __restrict__ w, int V,
     int K, int pad_s, FastDiv pdiv, const float* __restrict__ row_scale, int gbs, int b0,
-    float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups) {
+    float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups, int gmain) {
   using C = DCfg<VT, WV, WB, NBT, NT, NS>;
   __shared__ __align__(1024) unsigned char smem[NS * C::STAGE];
 
@@ -304,17 +320,65 @@ __global__ __launch_bounds__(WV * WB * 64) void dma_kernel(
   const int wv = wave % WV, wb = wave / WV;
   const int s16 = lane & 15, kg = lane >> 4;
   const int P = gridDim.x;
-  const int g0 = int((long long)blockIdx.x * groups / P);
-  const int g1 = int((long long)(blockIdx.x + 1) * groups / P);
+  const int g0 = int((long long)blockIdx.x * gmain / P);
+  const int g1 = int((long long)(blockIdx.x + 1) * gmain / P);
   const int c0 = g0 * kFusedGroup, c1 = min(g1 * kFusedGroup, V);
   const int nsub = (c1 - c0 + VT - 1) / VT;
-  const int nks = Kp / 32;
-  const int total = nsub * nks;
+  const int nks = Kp / 32;  // even: Kp is a multiple of 64
+  const int nmain = nsub * nks;
+  // leftover items (region, row group), blockIdx.x, blockIdx.x + P, ...; each
+  // nks / 2 steps of two K blocks
+  const int lcol0 = gmain * kFusedGroup;
+  const int nitems = (C::ITEMS && lcol0 < V) ? (V - lcol0 + VT - 1) / VT * WB : 0;
+  const int nitm = int(blockIdx.x) < nitems ? (nitems - 1 - int(blockIdx.x)) / P + 1 : 0;
+  const int iks = nks / 2;
+  const int total = nmain + nitm * iks;
   if (total <= 0) return;
   const int rtiles = rows_pad / 16;
 
+  // item step q >= nmain: item id, its region's first column, first K block
+  auto item_at = [&](int q, int& v0, int& kb) {
+    const int id = int(blockIdx.x) + ((q - nmain) / iks) * P;
+    v0 = lcol0 + (id / WB) * VT;
+    kb = 2 * ((q - nmain) % iks);
+    return id % WB;
+  };
+
+  // this wave's copies of item step q: copies [0, 2 WINS) the weights of
+  // blocks kb and kb + 1, the rest the row group's fragments of both blocks
+  // (block, term, row tile), in slot order
+  auto issue_item = [&](int q) {
+    int v0, kb;
+    const int rg = item_at(q, v0, kb);
+    unsigned char* st = smem + (q % NS) * C::STAGE;
+    for (int i = wave; i < C::NINS; i += C::NW) {
+      if (i < 2 * C::WINS) {
+        const int blk = i / C::WINS, ks = kb + blk, ii = i - blk * C::WINS;
+        const int r = ii * C::RPI + lane / (64 / C::RPI);
+        const int p = lane % (64 / C::RPI);
+        const int c = p ^ (2 * (r & 7));
+        const int u = min(ks * 32 + r, K - 1);
+        const int h = pad_s ? u + int(fastdiv(uint32_t(u), pdiv)) : u;
+        const int col = min(v0 + c * 8, V - 8);
+        __builtin_amdgcn_global_load_lds(w + size_t(h) * V + col, (lds_void*)(st + i * 1024), 16, 0,
+                                         2 /* non-temporal */);
+      } else {
+        const int e = i - 2 * C::WINS;
+        const int ks = kb + e / (NT * C::BTW), t = (e / C::BTW) % NT;
+        const int rt = min(b0 / 16 + rg * C::BTW + e % C::BTW, rtiles - 1);
+        __builtin_amdgcn_global_load_lds(
+            act + (((size_t(t) * rtiles + rt) * (Kp / 32) + ks) * 64 + lane) * 8,
+            (lds_void*)(st + i * 1024), 16, 0, 0);
+      }
+    }
+  };
+
   // this wave's copies of step q into stage (q % NS)
   auto issue = [&](int q) {
+    if (C::ITEMS && q >= nmain) {
+      issue_item(q);
+      return;
+    }
     const int j = q / nks, ks = q % nks;
     const int v0 = c0 + j * VT;
     unsigned char* st = smem + (q % NS) * C::STAGE;
@@ -369,37 +433,25 @@ __global__ __launch_bounds__(WV * WB * 64) void dma_kernel(
     tr_addr[vt] = smem_base + tr_row * C::WPITCH + ch * 16 + 8 * (s16 & 3);
   }
 
-  for (int p = 0; p < NS - 1 && p < total; ++p) issue(p);
-  for (int q = 0; q < total; ++q) {
-    // this wave's copies of step q are done once at most those of the steps
-    // after it that are already issued are outstanding (copies complete in
-    // issue order); the barrier extends that to every wave, and also retires
-    // every wave's reads of step q - 1, whose stage step q + NS - 1 reuses
-    wait_steps<C::WAIT, NS - 2>(min(NS - 2, total - 1 - q));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (q + NS - 1 < total) issue(q + NS - 1);
-
-    const int j = q / nks, ks = q % nks;
-    const int v0 = c0 + j * VT, vend = min(v0 + VT, c1);
-    const int ntile = __builtin_amdgcn_readfirstlane((vend - v0 + 15) / 16 - wv * C::VTW);
-    const uint32_t soff = uint32_t((q % NS) * C::STAGE);
-    const unsigned char* st = smem + (q % NS) * C::STAGE;
+  // one 32-row K block of a stage: the weights at LDS byte aoff (read
+  // transposed), the wave's fragment (term t, row tile bt) at
+  // bsrc + (t tstride + bt) KiB; tiles past ntile are skipped
+  auto mma_block = [&](uint32_t aoff, const unsigned char* bsrc, int tstride, int ntile) {
     s16x4 alo[C::VTW], ahi[C::VTW];
 #pragma unroll
     for (int vt = 0; vt < C::VTW; ++vt) {
-      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(alo[vt]) : "v"(tr_addr[vt] + soff));
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(alo[vt]) : "v"(tr_addr[vt] + aoff));
       asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
                    : "=v"(ahi[vt])
-                   : "v"(tr_addr[vt] + soff), "i"(16 * C::WPITCH));
+                   : "v"(tr_addr[vt] + aoff), "i"(16 * C::WPITCH));
     }
     bf16x8 bfr[C::BTW][NT];
 #pragma unroll
     for (int bt = 0; bt < C::BTW; ++bt)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        bfr[bt][t] = *reinterpret_cast<const bf16x8*>(
-            st + C::WBYTES + ((t * NBT + wb * C::BTW + bt) * 64 + lane) * 16);
+        bfr[bt][t] =
+            *reinterpret_cast<const bf16x8*>(bsrc + ((t * tstride + bt) * 64 + lane) * 16);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int vt = 0; vt < C::VTW; ++vt) asm volatile("" : "+v"(alo[vt]), "+v"(ahi[vt]));
@@ -418,33 +470,79 @@ __global__ __launch_bounds__(WV * WB * 64) void dma_kernel(
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfr[bt][t], acc[vt][bt], 0, 0, 0);
       }
     }
-    asm volatile("" ::: "memory");
-    if (ks == nks - 1) {
+  };
+
+  // the wave's finished tiles of columns [v0, vend): scaled logits, the
+  // maxima of groups below gend, and cleared accumulators
+  auto flush = [&](int v0, int vend, int gend) {
 #pragma unroll
-      for (int bt = 0; bt < C::BTW; ++bt) {
-        const int b = b0 + (wb * C::BTW + bt) * 16 + s16;
-        const float sc = scale[bt];
-        uint32_t gm = 0;
+    for (int bt = 0; bt < C::BTW; ++bt) {
+      const int b = b0 + (wb * C::BTW + bt) * 16 + s16;
+      const float sc = scale[bt];
+      uint32_t gm = 0;
 #pragma unroll
-        for (int vt = 0; vt < C::VTW; ++vt) {
-          const int v = v0 + (wv * C::VTW + vt) * 16 + 4 * kg;
-          const float4 o = make_float4(acc[vt][bt][0] * sc, acc[vt][bt][1] * sc,
-                                       acc[vt][bt][2] * sc, acc[vt][bt][3] * sc);
-          if (b < gbs && v < vend) {
-            *reinterpret_cast<float4*>(logits + size_t(b) * V + v) = o;
-            gm = max(gm, max(max(float_key(o.x), float_key(o.y)),
-                             max(float_key(o.z), float_key(o.w))));
-          }
-          if (vt % 4 == 3) {
-            gm = max(gm, (uint32_t)__shfl_xor((int)gm, 16, 64));
-            gm = max(gm, (uint32_t)__shfl_xor((int)gm, 32, 64));
-            const int g = (v0 + (wv * C::VTW + vt - 3) * 16) / kFusedGroup;
-            if (gkey && kg == 0 && b < gbs && g < g1) gkey[size_t(b) * groups + g] = gm;
-            gm = 0;
-          }
-          acc[vt][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int vt = 0; vt < C::VTW; ++vt) {
+        const int v = v0 + (wv * C::VTW + vt) * 16 + 4 * kg;
+        const float4 o = make_float4(acc[vt][bt][0] * sc, acc[vt][bt][1] * sc,
+                                     acc[vt][bt][2] * sc, acc[vt][bt][3] * sc);
+        if (b < gbs && v < vend) {
+          *reinterpret_cast<float4*>(logits + size_t(b) * V + v) = o;
+          gm = max(gm, max(max(float_key(o.x), float_key(o.y)),
+                           max(float_key(o.z), float_key(o.w))));
         }
+        if (vt % 4 == 3) {
+          gm = max(gm, (uint32_t)__shfl_xor((int)gm, 16, 64));
+          gm = max(gm, (uint32_t)__shfl_xor((int)gm, 32, 64));
+          const int g = (v0 + (wv * C::VTW + vt - 3) * 16) / kFusedGroup;
+          if (gkey && kg == 0 && b < gbs && g < gend) gkey[size_t(b) * groups + g] = gm;
+          gm = 0;
+        }
+        acc[vt][bt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+    }
+  };
+
+  for (int p = 0; p < NS - 1 && p < total; ++p) issue(p);
+  for (int q = 0; q < nmain; ++q) {
+    // this wave's copies of step q are done once at most those of the steps
+    // after it that are already issued are outstanding (copies complete in
+    // issue order); the barrier extends that to every wave, and also retires
+    // every wave's reads of step q - 1, whose stage step q + NS - 1 reuses
+    wait_steps<C::WAIT, NS - 2>(min(NS - 2, total - 1 - q));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (q + NS - 1 < total) issue(q + NS - 1);
+
+    const int j = q / nks, ks = q % nks;
+    const int v0 = c0 + j * VT, vend = min(v0 + VT, c1);
+    const int ntile = __builtin_amdgcn_readfirstlane((vend - v0 + 15) / 16 - wv * C::VTW);
+    const uint32_t soff = uint32_t((q % NS) * C::STAGE);
+    const unsigned char* st = smem + (q % NS) * C::STAGE;
+    mma_block(soff, st + C::WBYTES + wb * C::BTW * 1024, NBT, ntile);
+    asm volatile("" ::: "memory");
+    if (ks == nks - 1) flush(v0, vend, g1);
+  }
+
+  // leftover item steps: only the item's row group computes, blocks kb and
+  // kb + 1 in that order, so every element accumulates its K in order
+  if constexpr (C::ITEMS) {
+    for (int q = nmain; q < total; ++q) {
+      wait_steps<C::WAIT, NS - 2>(min(NS - 2, total - 1 - q));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (q + NS - 1 < total) issue(q + NS - 1);
+      int v0, kb;
+      const int rg = item_at(q, v0, kb);
+      if (wb != rg) continue;
+      const int vend = min(v0 + VT, V);
+      const int ntile = __builtin_amdgcn_readfirstlane((vend - v0 + 15) / 16 - wv * C::VTW);
+      const uint32_t soff = uint32_t((q % NS) * C::STAGE);
+      const unsigned char* st = smem + (q % NS) * C::STAGE + 2 * C::WBYTES;
+#pragma nounroll
+      for (int blk = 0; blk < 2; ++blk)
+        mma_block(soff + blk * C::WBYTES, st + blk * NT * C::BTW * 1024, C::BTW, ntile);
+      asm volatile("" ::: "memory");
+      if (kb == nks - 2) flush(v0, vend, groups);
     }
   }
 }
@@ -470,8 +568,10 @@ hipError_t launch_dma(const uint16_t* act, int rows_pad, int Kp, const uint16_t*
   const FastDiv pdiv = make_fastdiv(pad_s > 1 ? uint32_t(pad_s - 1) : 1u);
   const int groups = (V + kFusedGroup - 1) / kFusedGroup;
   const int P = min(groups, slots);
+  // groups dealt as whole ranges; the rest go out as leftover items
+  const int gmain = DCfg<VT, WV, WB, NBT, NT, NS>::ITEMS ? groups / P * P : groups;
   hipLaunchKernelGGL(kern, dim3(P), dim3(WV * WB * 64), 0, st, act, rows_pad, Kp, w, V, K, pad_s,
-                     pdiv, row_scale, gbs, b0, logits, gkey, groups);
+                     pdiv, row_scale, gbs, b0, logits, gkey, groups, gmain);
   return hipGetLastError();
 }
 

@@ -145,14 +145,18 @@ def test_lm_head_duplicate_columns_and_batch_invariance(big, H):
 
 
 @pytest.mark.parametrize("page", [False, True])
-def test_lm_head_persistent_uneven_groups(page):
+@pytest.mark.parametrize("gbs,H", [(160, 256), (150, 200)])
+def test_lm_head_persistent_uneven_groups(page, gbs, H):
     """Above 128 rows, on a vocabulary whose 64-column groups do not divide
-    over the persistent kernel's workgroups (some of them take a partial
-    extra sub-tile), the logits meet the parity bar and columns duplicated
-    between the whole sub-tiles and the partial ones give bitwise equal
-    logits (every element takes its full K in order)."""
-    rng = np.random.default_rng(11 + page)
-    gbs, H, V = 160, 256, 196928  # 3077 groups over 256 workgroups
+    over the persistent kernel's workgroups (the groups past the even split
+    go out as leftover items of one region x one row group with two terms,
+    as a partial extra sub-tile with one), the logits meet the parity bar
+    and columns duplicated between the whole sub-tiles and the leftover ones
+    give bitwise equal logits (every element takes its full K in order).
+    150 rows leave one row group empty and one partly filled; K = 200 pads
+    to 256 with clamped weight rows."""
+    rng = np.random.default_rng(11 + page + gbs)
+    V = 196928  # 3077 groups over 256 workgroups: 5 left over, one partial region
     w = bf16_bits(rng.standard_normal((H, V)) * 0.05)
     cut = 3072 * 64
     src = rng.choice(cut, 48, replace=False)
