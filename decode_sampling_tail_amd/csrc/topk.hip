@@ -314,6 +314,37 @@ __device__ inline uint32_t mirror_key(uint32_t key) {
   return float_key(__uint_as_float(bf16_rne_bits(bits) << 16));
 }
 
+// One batch of candidate float4 slots f0 + u * kSelThreads (gs >= 4, per =
+// gs / 4 = 2^lg slots a group, total slots): every group id is read from LDS
+// first, then every load is issued, from a clamped slot, through a global
+// pointer, with no branch between the loads.  (The helpers that call this
+// are not always inlined; through the generic row pointer they issued
+// generic loads, which count in the LDS wait counter too.  Timing did not
+// change.)  in[u] tells the slots that exist and lie below V.
+template <int NB>
+__device__ inline void load_candidates(const SelShared& s, const float* row, int V, int gs, int lg,
+                                       int total, int f0, float4 (&v)[NB], int (&e)[NB],
+                                       bool (&in)[NB]) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(1))) f32x4v gf32x4;
+  const int per = gs >> 2;
+  int grp[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int fi = f0 + u * kSelThreads;
+    grp[u] = int(s.act[(fi < total ? fi : total - 1) >> lg]);
+  }
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int fi = f0 + u * kSelThreads;
+    const int fc = fi < total ? fi : total - 1;
+    e[u] = grp[u] * gs + (fc & (per - 1)) * 4;
+    in[u] = fi < total && e[u] < V;
+    const f32x4v x = *(gf32x4*)(row + min(e[u], V - 4));  // V is a multiple of 8
+    v[u] = make_float4(x[0], x[1], x[2], x[3]);
+  }
+}
+
 // Visit every element of the candidate groups, kBatch float4 loads in flight
 // per thread.  f(in, key, e, bits) is called by all lanes of a wave the same
 // number of times (out-of-range slots have in == false).
@@ -326,21 +357,10 @@ __device__ inline void for_candidates(const SelShared& s, const float* row, int 
     const int lg = __ffs(per) - 1;
     const int total = nact * per;
     for (int w0 = wave_first; w0 < total; w0 += kBatch * kSelThreads) {
-      const int f0 = w0 + (tid & 63);
       float4 v[kBatch];
       int e[kBatch];
       bool in[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int fi = f0 + u * kSelThreads;
-        in[u] = false;
-        e[u] = 0;
-        if (fi < total) {
-          e[u] = int(s.act[fi >> lg]) * gs + (fi & (per - 1)) * 4;
-          in[u] = e[u] < V;
-        }
-        v[u] = in[u] ? *reinterpret_cast<const float4*>(row + e[u]) : make_float4(0, 0, 0, 0);
-      }
+      load_candidates(s, row, V, gs, lg, total, w0 + (tid & 63), v, e, in);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const uint32_t bx = rank_bits<MIRROR>(v[u].x, fold), by = rank_bits<MIRROR>(v[u].y, fold);
@@ -355,13 +375,11 @@ __device__ inline void for_candidates(const SelShared& s, const float* row, int 
     const int total = nact * gs;
     for (int w0 = wave_first; w0 < total; w0 += kSelThreads) {
       const int fi = w0 + (tid & 63);
-      int e = 0;
-      bool in = false;
-      if (fi < total) {
-        e = int(s.act[fi / gs]) * gs + fi % gs;
-        in = e < V;
-      }
-      const uint32_t bx = rank_bits<MIRROR>(in ? row[e] : 0.0f, fold);
+      const int fc = fi < total ? fi : total - 1;
+      const int e = int(s.act[fc / gs]) * gs + fc % gs;
+      const bool in = fi < total && e < V;
+      const float x = *(const __attribute__((address_space(1))) float*)(row + min(e, V - 1));
+      const uint32_t bx = rank_bits<MIRROR>(in ? x : 0.0f, fold);
       f(in, float_key(__uint_as_float(bx)), e, bx);
     }
   }
@@ -393,21 +411,10 @@ __device__ inline void scan_candidates(SelShared& s, const float* row, int V, in
   const int lg = __ffs(per) - 1;
   const int total = nact * per;
   for (int w0 = wave_first; w0 < total; w0 += kScanBatch * kSelThreads) {
-    const int f0 = w0 + lane;
     float4 v[kScanBatch];
     int e[kScanBatch];
     bool in[kScanBatch];
-#pragma unroll
-    for (int u = 0; u < kScanBatch; ++u) {
-      const int fi = f0 + u * kSelThreads;
-      in[u] = false;
-      e[u] = 0;
-      if (fi < total) {
-        e[u] = int(s.act[fi >> lg]) * gs + (fi & (per - 1)) * 4;
-        in[u] = e[u] < V;
-      }
-      v[u] = in[u] ? *reinterpret_cast<const float4*>(row + e[u]) : make_float4(0, 0, 0, 0);
-    }
+    load_candidates(s, row, V, gs, lg, total, w0 + lane, v, e, in);
     uint32_t bits[kScanBatch * 4], mask = 0;
 #pragma unroll
     for (int u = 0; u < kScanBatch; ++u) {
