@@ -234,10 +234,11 @@ __global__ __launch_bounds__(WV * WB * 64, MINB) void mfma_kernel(
 // (global_load_lds_dwordx4) and an NS-stage LDS ring.
 //
 // The grid holds as many workgroups as fit on the device at once; workgroup
-// w owns the contiguous range of 64-column key groups [w G / P, (w + 1) G / P)
-// (G groups, P workgroups), so every workgroup gets the same number of
-// columns to within one group, and walks it in sub-tiles of VT columns (the
-// last one may be narrower), one K-step of 32 rows at a time.  The K-steps of
+// w owns the contiguous range of 64-column key groups [w G' / P,
+// (w + 1) G' / P) (P workgroups; G' is all G groups, or with leftover items,
+// below, the P floor(G / P) that divide evenly), so every workgroup gets the
+// same number of columns to within one group, and walks it in sub-tiles of
+// VT columns (the last one may be narrower), one K-step of 32 rows at a time.  The K-steps of
 // all its sub-tiles form one pipeline: the copies for step q + NS - 1 go out
 // while step q runs, without passing through registers, so NS - 1 steps of
 // memory latency are hidden; one barrier per step.  Wave (wv, wb) owns tiles
@@ -268,7 +269,10 @@ __global__ __launch_bounds__(WV * WB * 64, MINB) void mfma_kernel(
 // first half of the fragment slots, and the row group's fragments of both
 // blocks in the second half.  An item so takes half a pass's steps; only its
 // row group's waves run MFMAs and write outputs, and every element still
-// takes its full K in order, so the logits are the same bytes.
+// takes its full K in order, so the logits are the same bytes.  The item
+// steps continue the same pipeline in a loop of their own after the
+// whole-pass steps (one loop choosing the step kind at run time scheduled
+// the whole-pass steps worse).
 template <int VT, int WV, int WB, int NBT, int NT, int NS>
 struct DCfg {
   static constexpr int NW = WV * WB, NTH = NW * 64;
