@@ -145,20 +145,23 @@ def test_lm_head_duplicate_columns_and_batch_invariance(big, H):
 
 
 @pytest.mark.parametrize("page", [False, True])
-@pytest.mark.parametrize("gbs,H", [(160, 256), (150, 200)])
-def test_lm_head_persistent_uneven_groups(page, gbs, H):
+@pytest.mark.parametrize("gbs,H,V", [(160, 256, 196928), (150, 200, 196928), (129, 64, 16448),
+                                     (200, 96, 65600)])
+def test_lm_head_persistent_uneven_groups(page, gbs, H, V):
     """Above 128 rows, on a vocabulary whose 64-column groups do not divide
     over the persistent kernel's workgroups (the groups past the even split
     go out as leftover items of one region x one row group with two terms,
     as a partial extra sub-tile with one), the logits meet the parity bar
     and columns duplicated between the whole sub-tiles and the leftover ones
     give bitwise equal logits (every element takes its full K in order).
-    150 rows leave one row group empty and one partly filled; K = 200 pads
-    to 256 with clamped weight rows."""
+    150 and 129 rows leave one row group empty and one partly filled; K =
+    200 pads to 256 with clamped weight rows; K = 64 gives a single item
+    step.  Vocabularies: 3077 groups (5 left over on 256 workgroups, one
+    partial region), 257 (one left over) and 1025."""
     rng = np.random.default_rng(11 + page + gbs)
-    V = 196928  # 3077 groups over 256 workgroups: 5 left over, one partial region
     w = bf16_bits(rng.standard_normal((H, V)) * 0.05)
-    cut = 3072 * 64
+    groups = V // 64
+    cut = groups // 256 * 256 * 64  # columns before the leftover on 256 workgroups
     src = rng.choice(cut, 48, replace=False)
     dup = cut + rng.choice(V - cut, 48, replace=False)
     w[:, dup] = w[:, src]
