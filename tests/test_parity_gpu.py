@@ -272,6 +272,10 @@ def test_workload_parity(cid, run):
     (5, 300, 300, 8000, 64, False, synth.DT_BF16),   # ragged last slab
     (9, 640, 640, 2048, 1024, False, synth.DT_F32),  # k = TAIL_K_MAX, two lm_head passes
     (1, 128, 128, 64, 64, False, synth.DT_F32),      # k = V
+    # above 128 rows: the persistent lm_head, whose leftover items end in a
+    # partial group (V not a multiple of 64) and write its maximum
+    (140, 64, 64, 16456, 256, False, synth.DT_F32),
+    (136, 96, 96, 65608, 64, False, synth.DT_BF16),
 ])
 def test_forward_small_shapes(gbs, H, H_u, V, k, zp, dtype):
     rng = np.random.default_rng(V * 31 + k)
