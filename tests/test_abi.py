@@ -87,7 +87,7 @@ def test_rmsnorm_validation():
 
 def test_rmsnorm_pad_stride_two_is_valid_geometry():
     # H = 4, H_u = 2: groups of s = 2 lanes, lanes 1 and 3 are pad -- valid.  Only
-    # the validation verdict is checked here: a valid call would launch, so it is
+    # the validation outcome is checked here: a valid call would launch, so it is
     # made invalid afterwards by a null output to stop before any HIP call.
     assert rms(H=4, H_u=2, flags=dst.ZERO_PAD, y=NULL) == dst.ERR_INVALID_ARG
 
