@@ -207,10 +207,18 @@ def random_params(seed: int, gbs: int, greedy_rows: int = 0) -> np.ndarray:
     return p
 
 
-def make_config(cid: int) -> TailInputs:
+def make_config(cid: int, seed: int | None = None) -> TailInputs:
+    """Workload `cid`; `seed` (default: cid) draws its hidden rows, gamma and
+    sampling parameters (the weight has its own fixed seed)."""
+    inp = _make_config(cid, cid if seed is None else seed)
+    if seed is not None and seed != cid:
+        inp.name = f"{inp.name}_seed{seed}"
+    return inp
+
+
+def _make_config(cid: int, seed: int) -> TailInputs:
     s = CONFIG_SHAPES[cid]
     gbs, H, H_u, V, k = s["gbs"], s["H"], s["H_u"], s["V"], s["k"]
-    seed = cid
     if cid == 0:
         hidden = normal_f32(seed, S_HIDDEN, gbs * H).reshape(gbs, H)
         gamma = normal_f32(seed, S_GAMMA, H, 1.0, 0.1)

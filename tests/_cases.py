@@ -33,8 +33,8 @@ CDF_BAND = 1e-6
 
 # ------------------------------------------------------------------ workloads
 @functools.lru_cache(maxsize=None)
-def config(cid: int) -> synth.TailInputs:
-    inp = synth.make_config(cid)
+def config(cid: int, seed: int | None = None) -> synth.TailInputs:
+    inp = synth.make_config(cid, seed)
     if cid == 3:
         plant_ties(inp)
     return inp

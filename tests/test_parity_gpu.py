@@ -266,6 +266,30 @@ def test_workload_parity(cid, run):
     assert not check_sampler_on_gpu_candidates(out["tokens"], out["vals"], out["idx"], params)
 
 
+@pytest.mark.parametrize("cid,seed", [(2, 12), (3, 13), (4, 14)])
+def test_workload_parity_other_seeds(cid, seed):
+    """The workloads' shapes and distributions with other hidden rows, gamma
+    and sampling parameters (ties re-planted for the padded workload)."""
+    inp = config(cid, seed)
+    ref = oracle_tail(inp, 0)
+    _gpu_cache.clear()
+    g = to_gpu(inp)
+    out = run_forward(inp, g, 0)
+    del g
+    fails, rel, mx = check_logits(out["logits"], ref["logits"])
+    print(f"\nworkload {cid} seed {seed}: max rel-L2 {rel.max():.3e}, max abs {mx.max():.3e}")
+    assert not fails, fails
+    assert not check_topk_sets(out["idx"], ref["logits"], inp.k)
+    assert not check_topk_exact(out["vals"], out["idx"], out["logits"], inp.k)
+    params = inp.params[0]
+    fails, exempt, widened = check_tokens(out["tokens"], ref, params, out["logits"], inp.k)
+    assert not fails, fails
+    assert not check_sampler_on_gpu_candidates(out["tokens"], out["vals"], out["idx"], params)
+    if cid == 3:  # every planted pair is bitwise equal
+        pairs = inp.tie_pairs
+        assert np.array_equal(out["logits"][:, pairs[:, 0]], out["logits"][:, pairs[:, 1]])
+
+
 @pytest.mark.parametrize("gbs,H,H_u,V,k,zp,dtype", [
     (3, 256, 256, 1032, 256, False, synth.DT_F32),   # groups of 4 columns: separate group-max pass
     (2, 48, 45, 4096, 16, True, synth.DT_F16),       # pad lanes, fused 128-column groups
