@@ -118,8 +118,8 @@ int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int
  *                      logits[b,v] = row_scale[b] * sum_h y[b,h] * W[h,v],
  *                      the sum in fp32 over the real (non-pad) lanes.  By
  *                      default the activations are never rounded to a single
- *                      bf16: the weight-streaming path (gbs <= 4) uses them
- *                      as fp32; the matrix-core path (gbs > 4) splits each
+ *                      bf16: the weight-streaming path (gbs <= 3) uses them
+ *                      as fp32; the matrix-core path (gbs > 3) splits each
  *                      into two bf16 terms whose sum keeps it to 2^-17
  *                      relative.  With TAIL_PAGE_PRECISION each y[b,h] is
  *                      first rounded to bf16.
