@@ -603,8 +603,11 @@ hipError_t launch_terms(const uint16_t* act, int rows_pad, int Kp, const uint16_
                         uint32_t* gkey, void* part_ws, hipStream_t st) {
   const int kc_n = mfma_ksplit(V, Kp);
   float* part = static_cast<float*>(part_ws);
-  // a split K runs every chunk on the per-tile kernel (128-row chunks)
-  const int chunk = kc_n > 1 ? 128 : 256;
+  // a split K runs every chunk on the per-tile kernel (128-row chunks); so
+  // do two-term batches up to 192 rows, for which a 128-row chunk plus the
+  // rest costs less than the persistent kernel's 256-row chunk (with one
+  // term the persistent kernel stays ahead)
+  const int chunk = kc_n > 1 || (NT == 2 && gbs <= 192) ? 128 : 256;
   for (int b0 = 0; b0 < gbs; b0 += chunk) {
     const int rows = gbs - b0 < chunk ? gbs - b0 : chunk;
     const int nbt = (rows + 15) / 16;

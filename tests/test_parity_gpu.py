@@ -145,8 +145,8 @@ def test_lm_head_duplicate_columns_and_batch_invariance(big, H):
 
 
 @pytest.mark.parametrize("page", [False, True])
-@pytest.mark.parametrize("gbs,H,V", [(160, 256, 196928), (150, 200, 196928), (129, 64, 16448),
-                                     (200, 96, 65600)])
+@pytest.mark.parametrize("gbs,H,V", [(224, 256, 196928), (193, 200, 196928), (150, 200, 196928),
+                                     (129, 64, 16448), (250, 64, 16448), (200, 96, 65600)])
 def test_lm_head_persistent_uneven_groups(page, gbs, H, V):
     """Above 128 rows, on a vocabulary whose 64-column groups do not divide
     over the persistent kernel's workgroups (the groups past the even split
@@ -154,9 +154,10 @@ def test_lm_head_persistent_uneven_groups(page, gbs, H, V):
     as a partial extra sub-tile with one), the logits meet the parity bar
     and columns duplicated between the whole sub-tiles and the leftover ones
     give bitwise equal logits (every element takes its full K in order).
-    150 and 129 rows leave one row group empty and one partly filled; K =
-    200 pads to 256 with clamped weight rows; K = 64 gives a single item
-    step.  Vocabularies: 3077 groups (5 left over on 256 workgroups, one
+    193 rows leave the last row group one row; with one term (the two-term
+    path runs up to 192 rows in 128-row chunks on the per-tile kernel) 150
+    and 129 rows leave one row group empty and one partly filled; K = 200
+    pads to 256 with clamped weight rows; K = 64 gives a single item step.  Vocabularies: 3077 groups (5 left over on 256 workgroups, one
     partial region), 257 (one left over) and 1025."""
     rng = np.random.default_rng(11 + page + gbs)
     w = bf16_bits(rng.standard_normal((H, V)) * 0.05)
@@ -296,10 +297,12 @@ def test_workload_parity_other_seeds(cid, seed):
     (5, 300, 300, 8000, 64, False, synth.DT_BF16),   # ragged last slab
     (9, 640, 640, 2048, 1024, False, synth.DT_F32),  # k = TAIL_K_MAX, two lm_head passes
     (1, 128, 128, 64, 64, False, synth.DT_F32),      # k = V
-    # above 128 rows: the persistent lm_head, whose leftover items end in a
-    # partial group (V not a multiple of 64) and write its maximum
+    # above 192 rows: the persistent lm_head, whose leftover items end in a
+    # partial group (V not a multiple of 64) and write its maximum; 140 rows:
+    # a 128-row chunk and a 12-row chunk on the per-tile kernel
+    (200, 64, 64, 16456, 256, False, synth.DT_F32),
+    (240, 96, 96, 65608, 64, False, synth.DT_BF16),
     (140, 64, 64, 16456, 256, False, synth.DT_F32),
-    (136, 96, 96, 65608, 64, False, synth.DT_BF16),
 ])
 def test_forward_small_shapes(gbs, H, H_u, V, k, zp, dtype):
     rng = np.random.default_rng(V * 31 + k)
