@@ -1,0 +1,447 @@
+// lm_head contraction for batches of more than 128 rows, on the bf16 matrix
+// cores with v_mfma_f32_32x32x16_bf16 (GPT-OSS tail API page, parameter
+// "lm_head_weight_t": [H, V] bf16, already transposed and C-contiguous).
+//
+// logits[b, v] = row_scale[b] * sum_h (sum_t A_t[b, h]) * W[h, v]
+//
+// The activations arrive as NT bf16 terms (two by default, each the bf16
+// rounding of what the earlier terms left, so every MFMA product is exact;
+// one in the page-precision mode), stored by the activation producer as
+// ready B-operand fragments: one 1 KB fragment per (16-lane K block, term,
+// 32-row tile), lane 32 h + n holding row n at K lanes 8 h .. 8 h + 7.
+//
+// One call covers a chunk of 256 batch rows for the whole vocabulary, with
+// one persistent workgroup per CU.  The vocabulary is cut into 32-column
+// blocks and the blocks into npass * P tiles of equal width (to within one
+// block, at most MB blocks); workgroup w takes tiles w, w + P, w + 2P, ...,
+// so at any time the P workgroups read one contiguous column range of every
+// weight row (whole DRAM pages together: measured 6.9 TB/s for the weight
+// stream alone against 5.3 TB/s with contiguous per-workgroup ranges).
+//
+// A workgroup has 8 waves, two per SIMD.  Wave w owns rows 64 (w % 4) ..
+// + 63 of the chunk and the first (w < 4) or second half of the tile's
+// blocks, in accumulators of 32 x 32.  Per K-step of 16 hidden lanes the
+// tile's weight [16 x 32 W] goes to an LDS ring of NSW stages, NSW - 1 steps
+// ahead, and the step's activation fragments (256 rows x NT terms) to a ring
+// of NSA stages, NSA - 1 steps ahead, by direct global-to-LDS copies: waves
+// 0-3 copy the weight, waves 4-7 the activations, so each wave waits only on
+// one stream (vector memory operations complete in issue order per wave: one
+// wave carrying both the slow weight stream and the fast activation stream
+// made the fast one wait for the slow one, 320 us against 227 us for the
+// data movement of one gbs-256 call).  One barrier per step publishes the
+// stage and retires the reads of the stage the next copies overwrite; it is
+// the bare s_barrier, since a workgroup fence before it would drain every
+// copy in flight.  The copies are issued as inline assembly: a compiler that
+// sees them would make every LDS read of the wave wait for every copy in
+// flight.  They write only LDS, so no register of the wave is pending.
+//
+// The two waves of a SIMD are staggered by half a step: between two barriers
+// waves 0-3 read the step's operands and then run its MFMAs, while waves
+// 4-7 first run the MFMAs of the operands they read before the barrier and
+// then read the step's; so one wave's LDS reads overlap the other's MFMAs
+// and the matrix core of the SIMD stays busy.  (Reading and then multiplying
+// in every wave cost 429 us against a 240 us MFMA floor.)
+//
+// LDS layouts: a weight stage holds 16 rows of 32 MB columns at a row pitch
+// of 64 MB bytes padded to 64 mod 256, so the 8 row segments that 32 lanes of
+// a transposing read touch fall in distinct 32-byte bank groups.  The weight
+// operand of a block comes from two ds_read_b64_tr_b16: in each 16-lane group
+// g of the wave, lane s supplies row 8 (g / 2) + s / 4 (+4 for the second
+// read), columns 16 (g % 2) + 4 (s % 4) .. + 3 of the block, and receives
+// column 16 (g % 2) + s at K lanes 8 (g / 2) .. + 7: the natural K order of
+// the activation fragments, which an activation stage holds as copied (1 KB
+// each, read back linearly).
+//
+// Epilogue (after a tile's last K-step): accumulator register 4 i + e of lane
+// l holds column 8 i + 4 (l / 32) + e of the block for row l % 32, so each
+// lane stores float4s; the 64-column key groups' maxima go to gkey (a plain
+// store when both 32-column blocks of the group belong to the wave, an atomic
+// maximum into the cleared entry when the group straddles two halves or two
+// tiles).
+//
+// Determinism: every output element is one fixed sequence of MFMAs (K-steps
+// in order, terms in order), the same for every column and row.
+#include "tail_internal.h"
+
+namespace tail {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+template <int N>
+__device__ inline void wait_vm() {
+  // vmcnt field split over bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most PER * n of this wave's vector memory operations are
+// outstanding (0 <= n <= N, wave-uniform).
+template <int PER, int N>
+__device__ inline void wait_copies(int n) {
+  if constexpr (N <= 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= N) wait_vm<PER * N>();
+    else wait_copies<PER, N - 1>(n);
+  }
+}
+
+template <int NT, int MB, int NSW, int NSA>
+struct RCfg {
+  static constexpr int NB = 2;                           // 32-row tiles per wave
+  static constexpr int RT = 4 * NB;                      // row tiles per chunk (256 rows)
+  static constexpr int WPITCH = MB * 64 + ((64 - (MB * 64) % 256) + 256) % 256;
+  static constexpr int WCH = WPITCH / 16;                // 16-byte chunks per weight row
+  static constexpr int WSTAGE = 16 * WPITCH;
+  static constexpr int WCOP = WSTAGE / 1024;             // weight copies per step
+  static constexpr int WPER = (WCOP + 3) / 4;            // most weight copies of a wave
+  static constexpr int AFR = NT * RT;                    // activation fragments per step
+  static constexpr int APER = AFR / 4;                   // activation copies per wave
+  static constexpr int ASTAGE = AFR * 1024;
+  static constexpr int LDS = NSW * WSTAGE + NSA * ASTAGE;
+  static constexpr int HB = (MB + 1) / 2;                // most blocks of a half
+  static_assert(WSTAGE % 1024 == 0 && WPITCH % 256 == 64 && AFR % 4 == 0 && NSW >= 2 &&
+                    NSA >= 2 && WPER * (NSW - 2) < 64 && APER * (NSA - 2) < 64 &&
+                    LDS <= 160 * 1024,
+                "tile");
+};
+
+// Shared geometry of one call: the tiles of workgroup wg.
+struct RowsGeom {
+  int P, wg, nblk, tbase, textra, ntl, nks, total;
+  __device__ __forceinline__ RowsGeom(int V, int Kp, int npass) {
+    P = gridDim.x;
+    wg = blockIdx.x;
+    nblk = (V + 31) / 32;
+    const int ntiles = P * npass;
+    tbase = nblk / ntiles;
+    textra = nblk % ntiles;
+    // tiles j = 0 .. ntl - 1 are tiles j P + wg (widths do not grow with the
+    // tile index, so the non-empty ones come first)
+    ntl = 0;
+    while (ntl < npass && tbase + ((ntl * P + wg) < textra ? 1 : 0) > 0) ++ntl;
+    nks = Kp / 16;
+    total = ntl * nks;
+  }
+  __device__ __forceinline__ void tile(int j, int& start, int& width) const {
+    const int t = j * P + wg;
+    width = tbase + (t < textra ? 1 : 0);
+    start = t * tbase + (t < textra ? t : textra);
+  }
+};
+
+// lgkmcnt(0) only (vmcnt and expcnt left at their maximum)
+__device__ inline void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ inline void step_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One direct copy of 16 bytes per lane from global memory into LDS at
+// lds_addr + 16 lane (lds_addr wave-uniform).  The copy takes its LDS address
+// from m0, which the statement sets itself; no other code of this kernel uses
+// m0 (it is a reserved register, so the clobber only documents the write).
+template <bool NONTEMPORAL>
+__device__ inline void copy_to_lds(const void* gptr, uint32_t lds_addr) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  if constexpr (NONTEMPORAL)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(gptr), "s"(m0) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gptr), "s"(m0) : "memory", "m0");
+}
+
+// The copies of one wave: the weight (waves 0-3) or the activations (4-7).
+template <typename C, int NT, int NSW, int NSA>
+struct Copier {
+  const RowsGeom& G;
+  uint32_t wring, aring;  // LDS byte addresses of the rings
+  int wave, lane;
+  const uint16_t* __restrict__ act;
+  int nrt;
+  const uint16_t* __restrict__ w;
+  int V, K, pad_s;
+  FastDiv pdiv;
+  int b0;
+
+  // this wave's copies of step q (of all the wave's steps)
+  __device__ __forceinline__ void issue(int q) const {
+    const int j = q / G.nks, ks = q % G.nks;
+    if (wave < 4) {
+      int start, width;
+      G.tile(j, start, width);
+      const uint32_t st = wring + uint32_t((q % NSW) * C::WSTAGE);
+#pragma unroll
+      for (int c = 0; c < C::WPER; ++c) {
+        const int ci = wave + 4 * c;  // copies wave, wave + 4, ...
+        if (ci < C::WCOP) {
+          const int i = ci * 64 + lane;  // 16-byte chunk of the stage
+          const int r = i / C::WCH, cc = i % C::WCH;
+          const int u = min(ks * 16 + r, K - 1);
+          const int h = pad_s ? u + int(fastdiv(uint32_t(u), pdiv)) : u;
+          const int col = min(start * 32 + cc * 8, V - 8);
+          // lanes past the tile's width stay idle (every copy of 64 chunks
+          // spans a whole row, so some of its lanes always copy)
+          if (cc < 4 * width) copy_to_lds<true>(w + size_t(h) * V + col, st + uint32_t(ci * 1024));
+        }
+      }
+    } else {
+      const uint32_t st = aring + uint32_t((q % NSA) * C::ASTAGE);
+#pragma unroll
+      for (int c = 0; c < C::APER; ++c) {
+        const int f = (wave - 4) * C::APER + c;  // fragment (term f / RT, row tile f % RT)
+        const int t = f / C::RT, rt = min(b0 / 32 + f % C::RT, nrt - 1);
+        copy_to_lds<false>(act + (((size_t(ks) * NT + t) * nrt + rt) * 64 + lane) * 8,
+                           st + uint32_t(f * 1024));
+      }
+    }
+  }
+  __device__ __forceinline__ int ahead() const { return wave < 4 ? NSW - 1 : NSA - 1; }
+  // this wave's copies of step q have landed once at most those of the steps
+  // issued after it are outstanding
+  __device__ __forceinline__ void wait(int q) const {
+    if (wave < 4) {
+      // waves whose last copy slot is empty issue one copy fewer per step
+      if (wave + 4 * (C::WPER - 1) < C::WCOP)
+        wait_copies<C::WPER, NSW - 2>(min(NSW - 2, G.total - 1 - q));
+      else
+        wait_copies<C::WPER - 1, NSW - 2>(min(NSW - 2, G.total - 1 - q));
+    } else {
+      wait_copies<C::APER, NSA - 2>(min(NSA - 2, G.total - 1 - q));
+    }
+  }
+  // the start of a step: this wave's copies of it landed and its reads of the
+  // previous one done, then the barrier
+  __device__ __forceinline__ void step(int q) const {
+    wait(q);
+    wait_lds();
+    step_barrier();
+  }
+  // the end of a step's work: the copies NS - 1 steps ahead.  Issued after
+  // the step's reads and MFMAs, since an issue that the memory pipeline does
+  // not accept at once stalls the wave's next instructions (measured: 4.5%
+  // faster than issuing right after the barrier).
+  __device__ __forceinline__ void refill(int q) const {
+    if (q + ahead() < G.total) issue(q + ahead());
+  }
+};
+
+// One wave's part of one tile (steps q0 .. q0 + nks - 1): WC blocks starting
+// at block cb0 of the tile, rows 64 rg .. 64 rg + 63.  LAG: the wave runs each
+// step's MFMAs after the next barrier (see above).
+template <typename C, typename CP, int NT, int NSW, int NSA, int WC, bool LAG>
+__device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, const lds_u8* aring,
+                                          int rg, int lane, int q0, int blk0, int cb0, int tstart,
+                                          int twidth, const float (&scale)[2], int b0, int gbs,
+                                          int V, float* __restrict__ logits,
+                                          uint32_t* __restrict__ gkey, int groups) {
+  constexpr int NB = C::NB;
+  const int g = lane >> 4, s = lane & 15;
+  const int tr_off = (8 * (g >> 1) + (s >> 2)) * C::WPITCH + 32 * (g & 1) + 8 * (s & 3) + cb0 * 64;
+  const int b_off = (rg * NB * 64 + lane) * 16;
+  const int nks = cp.G.nks;
+
+  f32x16 acc[WC][NB];
+#pragma unroll
+  for (int c = 0; c < WC; ++c)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[c][nb][e] = 0.0f;
+
+  bf16x8 bop[NB][NT], aop[WC];
+  auto read = [&](int q) {
+    const lds_u8* wst = wring + (q % NSW) * C::WSTAGE + tr_off;
+    const lds_u8* ast = aring + (q % NSA) * C::ASTAGE + b_off;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        bop[nb][t] = *reinterpret_cast<const lds_bf16x8*>(ast + (t * C::RT + nb) * 1024);
+#pragma unroll
+    for (int c = 0; c < WC; ++c) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(wst + c * 64));
+      const s16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(wst + c * 64 + 4 * C::WPITCH));
+      const s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      aop[c] = __builtin_bit_cast(bf16x8, av);
+    }
+  };
+  auto mma = [&]() {
+#pragma unroll
+    for (int c = 0; c < WC; ++c)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[c][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[c], bop[nb][t], acc[c][nb], 0, 0, 0);
+  };
+
+  for (int ks = 0; ks < nks; ++ks) {
+    const int q = q0 + ks;
+    cp.step(q);
+    if constexpr (LAG) {
+      if (ks > 0) mma();
+      read(q);
+    } else {
+      read(q);
+      mma();
+    }
+    cp.refill(q);
+  }
+  if constexpr (LAG) mma();
+
+  // epilogue: scaled logits, key-group maxima
+  const int nblk = cp.G.nblk;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int b = b0 + (rg * NB + nb) * 32 + (lane & 31);
+    const bool row_ok = b < gbs;
+    uint32_t prev = 0;  // maximum of the previous block
+#pragma unroll
+    for (int c = 0; c < WC; ++c) {
+      const int blk = blk0 + c;
+      uint32_t mx = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = blk * 32 + 8 * i + 4 * (lane >> 5);
+        const float4 o = make_float4(acc[c][nb][4 * i] * scale[nb], acc[c][nb][4 * i + 1] * scale[nb],
+                                     acc[c][nb][4 * i + 2] * scale[nb], acc[c][nb][4 * i + 3] * scale[nb]);
+        if (row_ok && v < V) {
+          *reinterpret_cast<float4*>(logits + size_t(b) * V + v) = o;
+          mx = max(mx, max(max(float_key(o.x), float_key(o.y)), max(float_key(o.z), float_key(o.w))));
+        }
+      }
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
+      if (gkey && row_ok && lane < 32) {
+        uint32_t* dst = gkey + size_t(b) * groups + blk / 2;
+        const bool even = (blk & 1) == 0;
+        // a one-block last group has no partner
+        const bool partner_here = even ? (c + 1 < WC || blk + 1 >= nblk) : (c > 0);
+        if (!partner_here) atomicMax(dst, mx);  // the group straddles two waves
+        else if (!even) *dst = max(prev, mx);   // both blocks here: one store
+        else if (blk + 1 >= nblk) *dst = mx;
+      }
+      prev = mx;
+    }
+  }
+  (void)tstart;
+  (void)twidth;
+}
+
+template <int NT, int MB, int NSW, int NSA>
+__global__ __launch_bounds__(512, 1) void rows_kernel(
+    const uint16_t* __restrict__ act, int nrt, int Kp, const uint16_t* __restrict__ w, int V, int K,
+    int pad_s, FastDiv pdiv, const float* __restrict__ row_scale, int gbs, int b0,
+    float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups, int npass) {
+  using C = RCfg<NT, MB, NSW, NSA>;
+  using CP = Copier<C, NT, NSW, NSA>;
+  __shared__ __align__(1024) unsigned char smem[C::LDS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const RowsGeom G(V, Kp, npass);
+  if (G.total == 0) return;  // the whole workgroup
+  lds_u8* const wring = (lds_u8*)smem;
+  lds_u8* const aring = wring + NSW * C::WSTAGE;
+  const uint32_t wring_addr = uint32_t(reinterpret_cast<uintptr_t>(wring));
+  const CP cp{G, wring_addr, wring_addr + uint32_t(NSW * C::WSTAGE), wave, lane, act, nrt, w, V,
+              K, pad_s, pdiv, b0};
+
+  const int rg = wave & 3, half = wave >> 2;
+  float scale[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int b = b0 + (rg * 2 + nb) * 32 + (lane & 31);
+    scale[nb] = (b < gbs && row_scale) ? row_scale[b] : 1.0f;
+  }
+  // the scales have arrived before the first copy is issued
+  wait_vm<0>();
+  for (int p = 0; p < cp.ahead() && p < G.total; ++p) cp.issue(p);
+
+  for (int j = 0; j < G.ntl; ++j) {
+    int start, width;
+    G.tile(j, start, width);
+    const int w0 = (width + 1) / 2;
+    const int cb0 = half ? w0 : 0, wc = half ? width - w0 : w0;
+    const int q0 = j * G.nks;
+#define TAIL_ROWS_PART(WW)                                                                       \
+  case WW:                                                                                       \
+    if constexpr (WW <= C::HB) {                                                                 \
+      if (half)                                                                                  \
+        tile_part<C, CP, NT, NSW, NSA, WW, true>(cp, wring, aring, rg, lane, q0, start + cb0, cb0, \
+                                                 start, width, scale, b0, gbs, V, logits, gkey,  \
+                                                 groups);                                        \
+      else                                                                                       \
+        tile_part<C, CP, NT, NSW, NSA, WW, false>(cp, wring, aring, rg, lane, q0, start + cb0,   \
+                                                  cb0, start, width, scale, b0, gbs, V, logits,  \
+                                                  gkey, groups);                                 \
+    }                                                                                            \
+    break;
+    switch (wc) {
+      case 0:  // a one-block tile leaves the second half empty: barriers only
+        for (int ks = 0; ks < G.nks; ++ks) {
+          cp.step(q0 + ks);
+          cp.refill(q0 + ks);
+        }
+        break;
+      TAIL_ROWS_PART(1) TAIL_ROWS_PART(2) TAIL_ROWS_PART(3) TAIL_ROWS_PART(4) TAIL_ROWS_PART(5)
+      default: break;
+    }
+#undef TAIL_ROWS_PART
+  }
+}
+
+template <int NT, int MB, int NSW, int NSA>
+hipError_t launch_rows_cfg(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V,
+                           int K, int pad_s, const float* row_scale, int gbs, int b0,
+                           float* logits, uint32_t* gkey, hipStream_t st) {
+  auto kern = rows_kernel<NT, MB, NSW, NSA>;
+  static std::once_flag once[kMaxDevices];
+  static int cus_cache[kMaxDevices];
+  const int cus = per_device(once, cus_cache, [&](int dev) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    return n;
+  });
+  const FastDiv pdiv = make_fastdiv(pad_s > 1 ? uint32_t(pad_s - 1) : 1u);
+  const int nblk = (V + 31) / 32;
+  const int P = nblk < cus ? nblk : cus;
+  const int npass = (nblk + P * MB - 1) / (P * MB);
+  const int groups = (V + kFusedGroup - 1) / kFusedGroup;
+  hipLaunchKernelGGL(kern, dim3(P), dim3(512), 0, st, act, rows_pad / 32, Kp, w, V, K, pad_s, pdiv,
+                     row_scale, gbs, b0, logits, gkey, groups, npass);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lm_head_rows(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,
+                               int V, int K, int pad_s, const float* row_scale, int gbs,
+                               float* logits, uint32_t* gkey, hipStream_t st) {
+  for (int b0 = 0; b0 < gbs; b0 += 256) {
+    hipError_t e;
+    if (nt == 2)
+      e = launch_rows_cfg<2, 9, 8, 4>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs, b0, logits,
+                                      gkey, st);
+    else if (nt == 1)
+      e = launch_rows_cfg<1, 9, 8, 6>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs, b0, logits,
+                                      gkey, st);
+    else
+      e = hipErrorInvalidValue;
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace tail

@@ -119,34 +119,55 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restric
 // t_2 = bf16(y - t_0 - t_1) (round to nearest even; each difference is exact
 // in fp32).
 //
-// Output layout: ready operand fragments of v_mfma_f32_16x16x32_bf16.  For
-// term t, row tile rt (rows 16 rt .. 16 rt + 15) and K block kb (unpadded
-// lanes 32 kb .. 32 kb + 31) one 1 KB fragment holds 64 lanes x 8 bf16; lane
-// 16 g + s carries row 16 rt + s at K slots 8 g .. 8 g + 7, and K slot
-// 8 g + j is unpadded lane 32 kb + 4 g + (j & 3) + 16 (j >> 2).  Fragments are
-// ordered (t, rt, kb), so the fragments of one row tile for consecutive K
-// blocks are contiguous.  Each thread produces one 16-byte lane (an "octet")
-// per term.
+// Output layout (L): ready operand fragments of the matrix-core kernels,
+// 1 KB each (64 lanes x 8 bf16).
+//  L = 0, v_mfma_f32_16x16x32_bf16: row tile rt = rows 16 rt .. 16 rt + 15,
+//    K block kb = unpadded lanes 32 kb .. 32 kb + 31; lane 16 g + s carries row
+//    16 rt + s at K slots 8 g .. 8 g + 7, and K slot 8 g + j is unpadded lane
+//    32 kb + 4 g + (j & 3) + 16 (j >> 2).  Ordered (term, row tile, K block),
+//    so the fragments of one row tile for consecutive K blocks are contiguous.
+//  L = 1, v_mfma_f32_32x32x16_bf16: row tile = rows 32 rt .. 32 rt + 31, K
+//    block = unpadded lanes 16 kb .. 16 kb + 15; lane 32 h + n carries row
+//    32 rt + n at unpadded lanes 16 kb + 8 h .. + 7 (natural order).  Ordered
+//    (K block, term, row tile), so all the fragments one K-step of the
+//    large-batch kernel reads are contiguous.
+// Each thread produces one 16-byte lane (an "octet") per term.  gz (may be
+// NULL): this row's [groups] entries are cleared (the matrix-core kernels
+// combine the maxima of the key groups that straddle two of their tiles
+// there with atomic maxima).
 __device__ inline uint16_t bf16_rne(float f) { return uint16_t(bf16_rne_bits(__float_as_uint(f))); }
 __device__ inline float bf16_val(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-template <int DT, int NT, bool NORM>
+template <int L>
+__device__ inline int octet_lane(int o, int j) {  // unpadded lane of slot j of octet o
+  if constexpr (L == 0) return 32 * (o / 4) + 4 * (o % 4) + (j & 3) + 16 * (j >> 2);
+  else return 8 * o + j;
+}
+
+template <int DT, int NT, bool NORM, int L>
 __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict__ src,
                                                          const float* __restrict__ gamma, int H,
                                                          int H_u, int K, int pad_s, FastDiv pdiv,
                                                          float eps, int deferred, int gbs,
                                                          int rows_pad, int Kp,
                                                          uint16_t* __restrict__ act,
-                                                         float* __restrict__ r_out) {
+                                                         float* __restrict__ r_out,
+                                                         uint32_t* __restrict__ gz, int groups) {
   __shared__ double s_part[kThreads / 64];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
-  const int nkb = Kp / 32, nrt = rows_pad / 16;
-  // 16-byte lane of octet o = 4 kb + g for term t
+  // 16-byte lane of octet o for term t
   auto lane_ptr = [&](int t, int o) {
-    const size_t frag = (size_t(t) * nrt + row / 16) * nkb + o / 4;
-    return reinterpret_cast<uint4*>(act + (frag * 64 + (o % 4) * 16 + row % 16) * 8);
+    if constexpr (L == 0) {  // o = 4 kb + g
+      const size_t frag = (size_t(t) * (rows_pad / 16) + row / 16) * (Kp / 32) + o / 4;
+      return reinterpret_cast<uint4*>(act + (frag * 64 + (o % 4) * 16 + row % 16) * 8);
+    } else {  // o = 2 kb + h
+      const size_t frag = (size_t(o / 2) * NT + t) * (rows_pad / 32) + row / 32;
+      return reinterpret_cast<uint4*>(act + (frag * 64 + (o % 2) * 32 + row % 32) * 8);
+    }
   };
+  if (gz && row < gbs)
+    for (int i = tid; i < groups; i += kThreads) gz[size_t(row) * groups + i] = 0u;
   if (row >= gbs) {
     for (int o = tid; o < Kp / 8; o += kThreads)
 #pragma unroll
@@ -163,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int o = o0 + tid + i * kThreads;
-        const int u = 32 * (o / 4) + 4 * (o % 4) + (j & 3) + 16 * (j >> 2);
+        const int u = octet_lane<L>(o, j);
         const int uc = u < K ? u : K - 1;
         const int h = pad_s ? uc + int(fastdiv(uint32_t(uc), pdiv)) : uc;
         xb[i][j] = load_bits<DT>(src, base + h);
@@ -175,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int o = o0 + tid + i * kThreads;
-        const int u = 32 * (o / 4) + 4 * (o % 4) + (j & 3) + 16 * (j >> 2);
+        const int u = octet_lane<L>(o, j);
         x[i][j] = u < K ? widen_bits<DT>(xb[i][j]) : 0.0f;
       }
   };
@@ -188,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
       uint16_t term[NT][8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int u = 32 * (o / 4) + 4 * (o % 4) + (j & 3) + 16 * (j >> 2);
+        const int u = octet_lane<L>(o, j);
         float y = 0.0f;
         if (u < K) {
           if constexpr (NORM) y = deferred ? x[i][j] * g[i][j] : (x[i][j] * r) * g[i][j];
@@ -287,27 +308,28 @@ hipError_t launch_rmsnorm(const void* hidden, int dtype, const float* gamma, int
 namespace tail {
 
 hipError_t launch_split(const void* src, int dtype, bool norm, const float* gamma, int gbs, int H,
-                        int H_u, int K, int pad_s, float eps, bool deferred, int nt, int rows_pad,
-                        int Kp, uint16_t* act, float* r, hipStream_t st) {
+                        int H_u, int K, int pad_s, float eps, bool deferred, int nt, int layout,
+                        int rows_pad, int Kp, uint16_t* act, float* r, uint32_t* gz, int groups,
+                        hipStream_t st) {
   const FastDiv pdiv = make_fastdiv(pad_s > 1 ? uint32_t(pad_s - 1) : 1u);
   dim3 grid(rows_pad), block(kThreads);
-#define TAIL_SPLIT(DT, NT, NORM)                                                              \
-  hipLaunchKernelGGL((split_kernel<DT, NT, NORM>), grid, block, 0, st, src, gamma, H, H_u, K, \
-                     pad_s, pdiv, eps, int(deferred), gbs, rows_pad, Kp, act, r)
+#define TAIL_SPLIT(DT, NT, NORM, L)                                                              \
+  hipLaunchKernelGGL((split_kernel<DT, NT, NORM, L>), grid, block, 0, st, src, gamma, H, H_u, K, \
+                     pad_s, pdiv, eps, int(deferred), gbs, rows_pad, Kp, act, r, gz, groups)
+#define TAIL_SPLIT_DT(NT, L)                    \
+  do {                                          \
+    if (!norm) TAIL_SPLIT(0, NT, false, L);     \
+    else if (dtype == 0) TAIL_SPLIT(0, NT, true, L); \
+    else if (dtype == 1) TAIL_SPLIT(1, NT, true, L); \
+    else TAIL_SPLIT(2, NT, true, L);            \
+  } while (0)
   // two terms (the default precision) or one (the page-precision mode)
-  if (nt == 2) {
-    if (!norm) TAIL_SPLIT(0, 2, false);
-    else if (dtype == 0) TAIL_SPLIT(0, 2, true);
-    else if (dtype == 1) TAIL_SPLIT(1, 2, true);
-    else TAIL_SPLIT(2, 2, true);
-  } else if (nt == 1) {
-    if (!norm) TAIL_SPLIT(0, 1, false);
-    else if (dtype == 0) TAIL_SPLIT(0, 1, true);
-    else if (dtype == 1) TAIL_SPLIT(1, 1, true);
-    else TAIL_SPLIT(2, 1, true);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (nt == 2 && layout == 0) TAIL_SPLIT_DT(2, 0);
+  else if (nt == 2 && layout == 1) TAIL_SPLIT_DT(2, 1);
+  else if (nt == 1 && layout == 0) TAIL_SPLIT_DT(1, 0);
+  else if (nt == 1 && layout == 1) TAIL_SPLIT_DT(1, 1);
+  else return hipErrorInvalidValue;
+#undef TAIL_SPLIT_DT
 #undef TAIL_SPLIT
   return hipGetLastError();
 }

@@ -62,7 +62,8 @@ SplitGeom split_geom(int gbs, int H, int H_u, int pad_s, unsigned flags) {
   SplitGeom g;
   g.K = pad_s ? H_u : H;
   g.Kp = (g.K + tail::kKStep - 1) / tail::kKStep * tail::kKStep;
-  g.rows_pad = (gbs + 15) / 16 * 16;
+  const int rt = tail::mfma_row_tile(gbs);
+  g.rows_pad = (gbs + rt - 1) / rt * rt;
   g.nt = tail::mfma_terms(gbs, flags & TAIL_PAGE_PRECISION);
   g.bytes = gbs > tail::kGemvMaxBatch ? size_t(g.nt) * g.rows_pad * g.Kp * 2 : 0;
   return g;
@@ -76,6 +77,7 @@ struct FwdLayout {
 size_t gemv_part(int gbs, int H, int H_u, int pad_s, int V) {
   const int K = pad_s ? H_u : H;
   if (gbs <= tail::kGemvMaxBatch) return tail::gemv_part_bytes(gbs, K, V);
+  if (tail::mfma_layout(gbs)) return 0;  // the large-batch kernel never splits K
   const int Kp = (K + tail::kKStep - 1) / tail::kKStep * tail::kKStep;
   return tail::mfma_part_bytes(gbs, Kp, V);
 }
@@ -133,12 +135,17 @@ hipError_t norm_lm_head(const void* hidden, int dtype, const float* gamma, const
                                     logits, gkey, part, st);
     return e;
   }
+  const int layout = tail::mfma_layout(gbs);
+  // the large-batch kernel combines straddling key groups into cleared entries
+  uint32_t* gz = layout ? gkey : nullptr;
   e = tail::launch_split(hidden, dtype, true, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, sg.nt,
-                         sg.rows_pad, sg.Kp, act, r, st);
-  if (e == hipSuccess)
-    e = tail::launch_lm_head_mfma(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
-                                  deferred ? r : nullptr, gbs, logits, gkey, part, st);
-  return e;
+                         layout, sg.rows_pad, sg.Kp, act, r, gz, (V + tail::kFusedGroup - 1) / tail::kFusedGroup, st);
+  if (e != hipSuccess) return e;
+  if (layout)
+    return tail::launch_lm_head_rows(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
+                                     deferred ? r : nullptr, gbs, logits, gkey, st);
+  return tail::launch_lm_head_mfma(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
+                                   deferred ? r : nullptr, gbs, logits, gkey, part, st);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TAIL_OK : TAIL_ERR_HIP; }
@@ -212,11 +219,15 @@ TAIL_API int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_
   // matrix-core path: the split activations, then the split-K partials
   if (int s = check_ws(ws, ws_bytes, align256(sg.bytes) + gemv_part(gbs, H, H_u, ps, V))) return s;
   uint16_t* act = (uint16_t*)ws;
+  const int layout = tail::mfma_layout(gbs);
   hipError_t e = tail::launch_split(y, TAIL_F32, false, nullptr, gbs, H, H_u, sg.K, ps, 0.0f, false,
-                                    sg.nt, sg.rows_pad, sg.Kp, act, nullptr, st);
+                                    sg.nt, layout, sg.rows_pad, sg.Kp, act, nullptr, nullptr, 0, st);
   if (e == hipSuccess)
-    e = tail::launch_lm_head_mfma(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps, row_scale, gbs,
-                                  logits, nullptr, (char*)ws + align256(sg.bytes), st);
+    e = layout ? tail::launch_lm_head_rows(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
+                                           row_scale, gbs, logits, nullptr, st)
+               : tail::launch_lm_head_mfma(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
+                                           row_scale, gbs, logits, nullptr,
+                                           (char*)ws + align256(sg.bytes), st);
   return hip_status(e);
 }
 

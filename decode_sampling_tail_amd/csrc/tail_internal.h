@@ -134,13 +134,23 @@ constexpr int kGemvMaxBatch = 3;
 constexpr int kKStep = 64;  // K granularity of the matrix-core path
 int mfma_terms(int gbs, bool page);  // bf16 terms per activation (1 in the page-precision mode)
 
+// Batches above this size run the lm_head on the 32x32x16 large-batch kernel
+// (lm_head_rows.hip), which reads its activations in fragment layout 1; the
+// others in layout 0 (lm_head_mfma.hip).
+constexpr int kRowsMinBatch = 129;
+inline int mfma_layout(int gbs) { return gbs >= kRowsMinBatch ? 1 : 0; }
+inline int mfma_row_tile(int gbs) { return mfma_layout(gbs) ? 32 : 16; }
+
 // Split (and, with norm, RMS-normalize) activations for the matrix-core path:
 // act holds nt * rows_pad * Kp bf16 bits over the K contraction lanes as 1 KB
-// MFMA operand fragments ordered (term, 16-row tile, 32-lane K block); r [gbs]
-// (norm only, may be NULL).
+// MFMA operand fragments ordered (term, row tile, K block) in the given layout
+// (0: 16-row tiles and 32-lane K blocks for v_mfma_f32_16x16x32_bf16, 1:
+// 32-row tiles and 16-lane K blocks for v_mfma_f32_32x32x16_bf16); r [gbs]
+// (norm only, may be NULL); gz [gbs, groups] (may be NULL) is cleared.
 hipError_t launch_split(const void* src, int dtype, bool norm, const float* gamma, int gbs, int H,
-                        int H_u, int K, int pad_s, float eps, bool deferred, int nt, int rows_pad,
-                        int Kp, uint16_t* act, float* r, hipStream_t st);
+                        int H_u, int K, int pad_s, float eps, bool deferred, int nt, int layout,
+                        int rows_pad, int Kp, uint16_t* act, float* r, uint32_t* gz, int groups,
+                        hipStream_t st);
 
 // Matrix-core lm_head; part_ws: mfma_part_bytes(gbs, Kp, V) bytes (256-byte
 // aligned) for the split-K partials of a narrow vocabulary.
@@ -149,6 +159,13 @@ size_t mfma_part_bytes(int gbs, int Kp, int V);
 hipError_t launch_lm_head_mfma(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,
                                int V, int H_u, int pad_s, const float* row_scale, int gbs,
                                float* logits, uint32_t* gkey, void* part_ws, hipStream_t st);
+
+// The large-batch lm_head (gbs >= kRowsMinBatch): act in layout 1 with
+// rows_pad a multiple of 32; gkey (may be NULL) must hold zeros where the
+// producer cleared it.
+hipError_t launch_lm_head_rows(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,
+                               int V, int K, int pad_s, const float* row_scale, int gbs,
+                               float* logits, uint32_t* gkey, hipStream_t st);
 
 // Split-K finish shared by the lm_head paths: logits[b, v] = row_scale[b] (or
 // 1) * sum over kc in order of part[kc][b][v]; gkey (may be NULL) as above.
