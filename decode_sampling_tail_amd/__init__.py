@@ -1,9 +1,11 @@
 """Python binding of the decode-tail HIP library (libtail.so).
 
 Argument marshalling only: every step of the tail runs in the library's HIP
-kernels.  Tensors must be contiguous CUDA (HIP) tensors on one device; the
-calls enqueue on torch's current stream of that device and never
-synchronize.  There is no CPU fallback: if the library is not built, loading
+kernels.  Tensors must be contiguous CUDA (HIP) tensors on one device, of the
+dtypes and shapes each call documents; every tensor argument (inputs,
+outputs and workspace) is checked before the call and a mismatch raises
+ValueError, so no kernel is handed a pointer of the wrong kind.  The calls
+enqueue on torch's current stream of that device and never synchronize.  There is no CPU fallback: if the library is not built, loading
 it raises.
 
 The names mirror the C entry points in include/tail.h:
@@ -81,12 +83,67 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _dev(t):
+def _dev(t, name="tensor"):
+    """The device of a tensor argument that must live on a GPU, contiguous."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
     if not t.is_cuda:
-        raise ValueError("decode_sampling_tail_amd needs GPU tensors")
+        raise ValueError(f"{name} must be a GPU tensor (got one on {t.device})")
     if not t.is_contiguous():
-        raise ValueError("decode_sampling_tail_amd needs contiguous tensors")
+        raise ValueError(f"{name} must be contiguous")
     return t.device
+
+
+def _check(t, name, dev, dtypes, shape=None, optional=False):
+    """Validate one tensor argument before any launch: on `dev`, contiguous,
+    one of `dtypes`, and of `shape` (None entries match any size).  A tensor
+    on another device, of another dtype or shape would hand the kernels a
+    pointer to memory of another kind or size."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    d = _dev(t, name)
+    if d != dev:
+        raise ValueError(f"{name} is on {d}, the call's tensors are on {dev}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected one of {tuple(dtypes)}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(e is not None and int(n) != int(e)
+                                        for n, e in zip(t.shape, shape)):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}; expected "
+                             f"{tuple('*' if e is None else e for e in shape)}")
+    return t
+
+
+def _f32():
+    return (_torch().float32,)
+
+
+def _i32():
+    return (_torch().int32,)
+
+
+def _u8():
+    return (_torch().uint8,)
+
+
+def _bf16_bits():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _hidden_dtypes():
+    torch = _torch()
+    return (torch.float32, torch.float16, torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _check_2d(t, name):
+    _dev(t, name)
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D (got shape {tuple(t.shape)})")
+    return t.shape
 
 
 def _stream(device):
@@ -102,13 +159,6 @@ def _hidden_dtype(t) -> int:
     if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
         return BF16
     raise ValueError(f"hidden dtype {t.dtype} is not fp32, fp16 or bf16")
-
-
-def _weight(t):
-    torch = _torch()
-    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-        raise ValueError("the lm_head weight must be bf16 (or its raw 16-bit pattern)")
-    return t
 
 
 def _call(name, *args):
@@ -127,11 +177,14 @@ def rmsnorm(hidden, gamma, H_u=None, eps=1e-5, zero_pad=False, deferred=False, o
             page=False):
     """tail_rmsnorm: returns (y [gbs,H] fp32, r [gbs] fp32)."""
     torch = _torch()
-    dev = _dev(hidden)
-    gbs, H = hidden.shape
+    gbs, H = _check_2d(hidden, "hidden")
+    dev = _check(hidden, "hidden", hidden.device, _hidden_dtypes()).device
+    _check(gamma, "gamma", dev, _f32(), (H,))
     H_u = H if H_u is None else H_u
     y = out_y if out_y is not None else torch.empty((gbs, H), dtype=torch.float32, device=dev)
     r = out_r if out_r is not None else torch.empty((gbs,), dtype=torch.float32, device=dev)
+    _check(y, "out_y", dev, _f32(), (gbs, H))
+    _check(r, "out_r", dev, _f32(), (gbs,))
     _call("tail_rmsnorm", _ptr(hidden), _hidden_dtype(hidden), _ptr(gamma), gbs, H, H_u, eps,
           _flags(zero_pad, deferred, page=page), _ptr(y), _ptr(r), _stream(dev))
     return y, r
@@ -140,15 +193,19 @@ def rmsnorm(hidden, gamma, H_u=None, eps=1e-5, zero_pad=False, deferred=False, o
 def lm_head(y, w_t, H_u=None, zero_pad=False, row_scale=None, out=None, ws=None, page=False):
     """tail_lm_head: logits [gbs,V] fp32 = row_scale * (y @ W)."""
     torch = _torch()
-    dev = _dev(y)
-    gbs, H = y.shape
-    V = w_t.shape[1]
+    gbs, H = _check_2d(y, "y")
+    dev = _check(y, "y", y.device, _f32()).device
+    _, V = _check_2d(w_t, "w_t")
+    _check(w_t, "w_t", dev, _bf16_bits(), (H, V))
+    _check(row_scale, "row_scale", dev, _f32(), (gbs,), optional=True)
     H_u = H if H_u is None else H_u
     logits = out if out is not None else torch.empty((gbs, V), dtype=torch.float32, device=dev)
+    _check(logits, "out", dev, _f32(), (gbs, V))
     if ws is None:
         n = workspace_size(gbs, H, H_u, V, 1, _flags(zero_pad, emit=True, page=page))
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
-    _call("tail_lm_head", _ptr(y), _ptr(_weight(w_t)), _ptr(row_scale), gbs, H, H_u, V,
+    _check(ws, "ws", dev, _u8(), (None,))
+    _call("tail_lm_head", _ptr(y), _ptr(w_t), _ptr(row_scale), gbs, H, H_u, V,
           _flags(zero_pad, page=page), _ptr(logits), _ptr(ws), ws.numel(), _stream(dev))
     return logits
 
@@ -157,17 +214,22 @@ def rmsnorm_lm_head(hidden, gamma, w_t, H_u=None, eps=1e-5, zero_pad=False, defe
                     out_r=None, ws=None, page=False):
     """tail_rmsnorm_lm_head: (logits [gbs,V] fp32, r [gbs] fp32)."""
     torch = _torch()
-    dev = _dev(hidden)
-    gbs, H = hidden.shape
-    V = w_t.shape[1]
+    gbs, H = _check_2d(hidden, "hidden")
+    dev = _check(hidden, "hidden", hidden.device, _hidden_dtypes()).device
+    _check(gamma, "gamma", dev, _f32(), (H,))
+    _, V = _check_2d(w_t, "w_t")
+    _check(w_t, "w_t", dev, _bf16_bits(), (H, V))
     H_u = H if H_u is None else H_u
     flags = _flags(zero_pad, deferred, page=page)
     logits = out if out is not None else torch.empty((gbs, V), dtype=torch.float32, device=dev)
     r = out_r if out_r is not None else torch.empty((gbs,), dtype=torch.float32, device=dev)
+    _check(logits, "out", dev, _f32(), (gbs, V))
+    _check(r, "out_r", dev, _f32(), (gbs,))
     if ws is None:
         n = workspace_size(gbs, H, H_u, V, 1, flags | EMIT_LOGITS)
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
-    _call("tail_rmsnorm_lm_head", _ptr(hidden), _hidden_dtype(hidden), _ptr(gamma), _ptr(_weight(w_t)),
+    _check(ws, "ws", dev, _u8(), (None,))
+    _call("tail_rmsnorm_lm_head", _ptr(hidden), _hidden_dtype(hidden), _ptr(gamma), _ptr(w_t),
           gbs, H, H_u, V, eps, flags, _ptr(logits), _ptr(r), _ptr(ws), ws.numel(), _stream(dev))
     return logits, r
 
@@ -178,12 +240,16 @@ def topk(logits, k, out_vals=None, out_idx=None, ws=None, mirror=False, nan_fold
     the stage-1 diagnostics, as raw u32) is given: (vals [gbs,k] fp32
     descending, idx [gbs,k] int32)."""
     torch = _torch()
-    dev = _dev(logits)
-    gbs, V = logits.shape
+    gbs, V = _check_2d(logits, "logits")
+    dev = _check(logits, "logits", logits.device, _f32()).device
     vals = out_vals if out_vals is not None else torch.empty((gbs, k), dtype=torch.float32, device=dev)
     idx = out_idx if out_idx is not None else torch.empty((gbs, k), dtype=torch.int32, device=dev)
+    _check(vals, "out_vals", dev, _f32(), (gbs, k))
+    _check(idx, "out_idx", dev, _i32(), (gbs, k))
+    _check(taps, "taps", dev, (torch.int32, torch.uint32), (gbs, 4), optional=True)
     if ws is None:
         ws = torch.empty(max(workspace_size(gbs, 1, 1, V, k, EMIT_LOGITS), 1), dtype=torch.uint8, device=dev)
+    _check(ws, "ws", dev, _u8(), (None,))
     if mirror or nan_fold or taps is not None:
         flags = (PAGE_PRECISION if mirror else 0) | (NAN_FOLD if nan_fold else 0)
         _call("tail_topk_ex", _ptr(logits), gbs, V, k, flags, _ptr(vals), _ptr(idx), _ptr(taps),
@@ -194,12 +260,20 @@ def topk(logits, k, out_vals=None, out_idx=None, ws=None, mirror=False, nan_fold
     return vals, idx
 
 
+def _check_params(params, dev, gbs):
+    _check_2d(params, "params")
+    return _check(params, "params", dev, _f32(), (gbs, None))
+
+
 def sample(vals, idx, params, out=None):
     """tail_sample: tokens [gbs] int32 from [gbs,3|4] params."""
     torch = _torch()
-    dev = _dev(vals)
-    gbs, k = vals.shape
+    gbs, k = _check_2d(vals, "vals")
+    dev = _check(vals, "vals", vals.device, _f32()).device
+    _check(idx, "idx", dev, _i32(), (gbs, k))
+    _check_params(params, dev, gbs)
     tokens = out if out is not None else torch.empty((gbs,), dtype=torch.int32, device=dev)
+    _check(tokens, "out", dev, _i32(), (gbs,))
     _call("tail_sample", _ptr(vals), _ptr(idx), gbs, k, _ptr(params), params.shape[1], _ptr(tokens),
           _stream(dev))
     return tokens
@@ -217,6 +291,8 @@ class Forward:
         self.eps = eps
         self.flags = _flags(zero_pad, deferred, emit_logits, page, nan_fold)
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         dev = self.device
         self.logits = torch.empty((gbs, V), dtype=torch.float32, device=dev) if emit_logits else None
         self.vals = torch.empty((gbs, k), dtype=torch.float32, device=dev)
@@ -228,8 +304,13 @@ class Forward:
         self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
 
     def __call__(self, hidden, gamma, w_t, params=None):
-        _dev(hidden)
-        _call("tail_forward", _ptr(hidden), _hidden_dtype(hidden), _ptr(gamma), _ptr(_weight(w_t)),
+        dev = self.device
+        _check(hidden, "hidden", dev, _hidden_dtypes(), (self.gbs, self.H))
+        _check(gamma, "gamma", dev, _f32(), (self.H,))
+        _check(w_t, "w_t", dev, _bf16_bits(), (self.H, self.V))
+        if params is not None:
+            _check_params(params, dev, self.gbs)
+        _call("tail_forward", _ptr(hidden), _hidden_dtype(hidden), _ptr(gamma), _ptr(w_t),
               self.gbs, self.H, self.H_u, self.V, self.k, self.eps, self.flags, _ptr(params),
               0 if params is None else params.shape[1], _ptr(self.logits), _ptr(self.vals),
               _ptr(self.idx), _ptr(self.tokens if params is not None else None), _ptr(self.ws),

@@ -10,18 +10,28 @@
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers, allocated, owned and freed by the
- *    caller.  The library allocates nothing, keeps no mutable global state,
- *    never synchronizes, and enqueues its kernels on `stream` (a hipStream_t
- *    passed as void*; NULL = the default stream).  Outputs are valid once the
- *    stream reaches that point.
+ *    caller.  The library allocates nothing, never synchronizes, and enqueues
+ *    its kernels on `stream` (a hipStream_t passed as void*; NULL = the
+ *    default stream).  Outputs are valid once the stream reaches that point.
+ *    Its only global state is a set of per-device caches of device queries
+ *    (compute-unit count, kernel occupancy, the raised LDS limit), each
+ *    filled once, thread-safely, the first time a call runs on that device
+ *    and never changed afterwards; no call's result depends on them beyond
+ *    the launch shape.
  *  - Arrays are C-contiguous (row-major) with the shapes given.
  *  - Every call validates its arguments on the host BEFORE any HIP call and
  *    returns a status code; on an error nothing is enqueued and no output is
  *    touched.  TAIL_ERR_HIP reports a launch error from the HIP runtime.
  *    Faults inside a kernel surface asynchronously, as for any HIP call.
- *  - Results are deterministic: the same inputs give the same bytes, and a
- *    logit never depends on the column's position or on the other rows of
- *    the batch within one lm_head path (no floating-point atomics).
+ *  - Results are deterministic: the same inputs give the same bytes (no
+ *    floating-point atomics).  Within one lm_head path a logit depends
+ *    neither on the column's position nor on the other rows of the batch, so
+ *    duplicated weight columns give bitwise-equal logits.  The path depends
+ *    on the batch size: weight streaming with fp32 FMAs up to 3 rows, the
+ *    16x16x32 matrix-core kernel from 4 to 128 rows, the 32x32x16 kernel
+ *    above; each sums in its own fixed order, so a row's logits may differ
+ *    in the last bits when the batch crosses 3/4 or 128/129 rows (each path
+ *    meets the same accuracy bar).
  *  - Calls on different streams may run concurrently as long as they do not
  *    share output or workspace memory.
  */
@@ -111,7 +121,11 @@ int tail_rmsnorm(const void* hidden, int dtype, const float* gamma, int gbs, int
  *   y         [gbs, H] fp32 normalized hidden rows (the output of tail_rmsnorm).
  *   w_t       [H, V]   bf16 raw bits, ALREADY TRANSPOSED and C-contiguous (V is
  *                      the fast axis), 16-byte aligned; V must be a multiple
- *                      of 8 (TAIL_ERR_UNSUPPORTED otherwise).
+ *                      of 8 (TAIL_ERR_UNSUPPORTED otherwise), so that every
+ *                      weight row starts 16-byte aligned for the 16-byte
+ *                      loads and copies of all lm_head kernels (every entry
+ *                      that takes V applies the same rule, and
+ *                      tail_workspace_size returns 0 for such a V).
  *   row_scale [gbs]    fp32 per-row factor applied to the finished sum (the
  *                      deferred rms scale), or NULL for none.
  *   logits    [gbs, V] fp32, 16-byte aligned:

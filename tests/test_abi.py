@@ -232,6 +232,10 @@ def test_workspace_size():
     assert ws(0, 16, 16, 64, 4, 0) == 0
     assert ws(1, 16, 16, 64, 65, 0) == 0
     assert ws(1, 3072, 2881, 64, 4, dst.ZERO_PAD) == 0
+    # a vocabulary that is not a multiple of 8 is unsupported everywhere: its
+    # weight rows would not start 16-byte aligned
+    for V in (201090, 1004, 12):
+        assert ws(4, 64, 64, V, 4, 0) == 0
     base = ws(8, 2880, 2880, 201088, 256, dst.EMIT_LOGITS)
     assert base % 256 == 0 and base > 0
     # without emitted logits the workspace holds them: +gbs*V*4 bytes (rounded)
