@@ -22,13 +22,15 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtail.so")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4, 5
+SCRATCH_BYTES = 64 << 20  # the static scratch of tail_forward_noalloc
 F32, F16, BF16 = 0, 1, 2
 EMIT_LOGITS, ZERO_PAD, DEFERRED_RMS, PAGE_PRECISION, NAN_FOLD = 1, 2, 4, 8, 16
 K_MAX, GBS_MAX, H_MAX = 1024, 4096, 65536
 
 EXPORTS = ("tail_rmsnorm", "tail_lm_head", "tail_rmsnorm_lm_head", "tail_topk", "tail_topk_ex",
-           "tail_sample", "tail_forward", "tail_workspace_size", "tail_status_string")
+           "tail_sample", "tail_forward", "tail_forward_noalloc", "tail_workspace_size",
+           "tail_status_string")
 
 _lib = None
 
@@ -54,12 +56,13 @@ def lib() -> ctypes.CDLL:
         L.tail_topk_ex.argtypes = [vp, i, i, i, u, vp, vp, vp, vp, sz, vp]
         L.tail_sample.argtypes = [vp, vp, i, i, vp, i, vp, vp]
         L.tail_forward.argtypes = [vp, i, vp, vp, i, i, i, i, i, f, u, vp, i, vp, vp, vp, vp, vp, sz, vp]
+        L.tail_forward_noalloc.argtypes = [vp, i, vp, vp, i, i, i, i, i, f, u, vp, i, vp, vp, vp, vp, vp]
         L.tail_workspace_size.argtypes = [i, i, i, i, i, u]
         L.tail_workspace_size.restype = sz
         L.tail_status_string.argtypes = [i]
         L.tail_status_string.restype = ctypes.c_char_p
         for name in ("tail_rmsnorm", "tail_lm_head", "tail_rmsnorm_lm_head", "tail_topk",
-                     "tail_topk_ex", "tail_sample", "tail_forward"):
+                     "tail_topk_ex", "tail_sample", "tail_forward", "tail_forward_noalloc"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -315,6 +318,24 @@ class Forward:
               0 if params is None else params.shape[1], _ptr(self.logits), _ptr(self.vals),
               _ptr(self.idx), _ptr(self.tokens if params is not None else None), _ptr(self.ws),
               self.ws.numel(), _stream(self.device))
+        return dict(logits=self.logits, vals=self.vals, idx=self.idx,
+                    tokens=self.tokens if params is not None else None)
+
+    def noalloc(self, hidden, gamma, w_t, params=None):
+        """The same call through tail_forward_noalloc: the library's static
+        scratch instead of this object's workspace (raises TailError with
+        ERR_SCRATCH_LIMIT when the shapes need more than SCRATCH_BYTES)."""
+        dev = self.device
+        _check(hidden, "hidden", dev, _hidden_dtypes(), (self.gbs, self.H))
+        _check(gamma, "gamma", dev, _f32(), (self.H,))
+        _check(w_t, "w_t", dev, _bf16_bits(), (self.H, self.V))
+        if params is not None:
+            _check_params(params, dev, self.gbs)
+        _call("tail_forward_noalloc", _ptr(hidden), _hidden_dtype(hidden), _ptr(gamma), _ptr(w_t),
+              self.gbs, self.H, self.H_u, self.V, self.k, self.eps, self.flags, _ptr(params),
+              0 if params is None else params.shape[1], _ptr(self.logits), _ptr(self.vals),
+              _ptr(self.idx), _ptr(self.tokens if params is not None else None),
+              _stream(self.device))
         return dict(logits=self.logits, vals=self.vals, idx=self.idx,
                     tokens=self.tokens if params is not None else None)
 

@@ -159,6 +159,8 @@ TAIL_API const char* tail_status_string(int status) {
     case TAIL_ERR_UNSUPPORTED: return "unsupported by this library";
     case TAIL_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case TAIL_ERR_HIP: return "HIP launch error";
+    case TAIL_ERR_SCRATCH_LIMIT:
+      return "the call needs more than the library's static scratch (TAIL_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -298,19 +300,22 @@ TAIL_API int tail_sample(const float* vals, const int32_t* idx, int gbs, int k,
       tail::launch_sample(vals, idx, gbs, k, params, ncols, tokens, (hipStream_t)stream));
 }
 
-TAIL_API int tail_forward(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t,
-                          int gbs, int H, int H_u, int V, int k, float eps, unsigned flags,
-                          const float* params, int ncols, float* logits, float* vals, int32_t* idx,
-                          int32_t* tokens, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+// Argument checks of tail_forward (pure host logic); the workspace is checked
+// by the caller.  ps receives the pad stride, L the workspace layout.
+int check_forward(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t, int gbs,
+                  int H, int H_u, int V, int k, float eps, unsigned flags, const float* params,
+                  int ncols, float* logits, float* vals, int32_t* idx, int32_t* tokens, int* ps,
+                  FwdLayout* L) {
   if (int s = check_shape(gbs, H, H_u)) return s;
   if (int s = check_vocab(V)) return s;
   if (int s = check_k(V, k)) return s;
   if (dtype != TAIL_F32 && dtype != TAIL_F16 && dtype != TAIL_BF16) return TAIL_ERR_INVALID_ARG;
   if (!(eps >= 0.0f) || !isfinite(eps)) return TAIL_ERR_INVALID_ARG;
   if (flags & ~kAllFlags) return TAIL_ERR_INVALID_ARG;
-  int ps = pad_stride(H, H_u, flags);
-  if (ps < 0) return TAIL_ERR_INVALID_ARG;
-  bool emit = flags & TAIL_EMIT_LOGITS;
+  *ps = pad_stride(H, H_u, flags);
+  if (*ps < 0) return TAIL_ERR_INVALID_ARG;
+  const bool emit = flags & TAIL_EMIT_LOGITS;
   if (!hidden || !gamma || !w_t || !vals || !idx) return TAIL_ERR_INVALID_ARG;
   if (emit && !logits) return TAIL_ERR_INVALID_ARG;
   if (params && (ncols != 3 && ncols != 4)) return TAIL_ERR_INVALID_ARG;
@@ -319,10 +324,16 @@ TAIL_API int tail_forward(const void* hidden, int dtype, const float* gamma, con
       !aligned(vals, 4) || !aligned(idx, 4) || (emit && !aligned(logits, 16)) ||
       (params && (!aligned(params, 4) || !aligned(tokens, 4))))
     return TAIL_ERR_INVALID_ARG;
-  FwdLayout L = forward_layout(gbs, H, H_u, ps, V, k, flags);
-  if (int s = check_ws(ws, ws_bytes, L.total)) return s;
+  *L = forward_layout(gbs, H, H_u, *ps, V, k, flags);
+  return TAIL_OK;
+}
 
-  hipStream_t st = (hipStream_t)stream;
+// The launches of tail_forward on a checked workspace of L.total bytes at ws.
+hipError_t forward_launch(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t,
+                          int gbs, int H, int H_u, int V, int k, float eps, unsigned flags, int ps,
+                          const float* params, int ncols, float* logits, float* vals, int32_t* idx,
+                          int32_t* tokens, const FwdLayout& L, void* ws, hipStream_t st) {
+  const bool emit = flags & TAIL_EMIT_LOGITS;
   char* base = (char*)ws;
   float* y = (float*)(base + L.y);
   float* r = (float*)(base + L.r);
@@ -343,5 +354,56 @@ TAIL_API int tail_forward(const void* hidden, int dtype, const float* gamma, con
   if (e == hipSuccess)
     e = tail::launch_select(lg, gbs, V, k, g, gk, flags & TAIL_PAGE_PRECISION, fold, vals, idx,
                             nullptr, params, ncols, tokens, st);
-  return hip_status(e);
+  return e;
+}
+
+// The static scratch of tail_forward_noalloc: one array per device, which
+// every call on that device shares.  Its device address comes from
+// hipGetSymbolAddress, once per device with that device current (the name
+// itself is a host-side stand-in, not a device address).
+constexpr size_t kScratchBytes = size_t(TAIL_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void* scratch_address() {
+  static std::once_flag once[tail::kMaxDevices];
+  static void* addr[tail::kMaxDevices];
+  return tail::per_device(once, addr, [](int) -> void* {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    return p;
+  });
+}
+}  // namespace
+
+TAIL_API int tail_forward(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t,
+                          int gbs, int H, int H_u, int V, int k, float eps, unsigned flags,
+                          const float* params, int ncols, float* logits, float* vals, int32_t* idx,
+                          int32_t* tokens, void* ws, size_t ws_bytes, void* stream) {
+  int ps;
+  FwdLayout L;
+  if (int s = check_forward(hidden, dtype, gamma, w_t, gbs, H, H_u, V, k, eps, flags, params, ncols,
+                            logits, vals, idx, tokens, &ps, &L))
+    return s;
+  if (int s = check_ws(ws, ws_bytes, L.total)) return s;
+  return hip_status(forward_launch(hidden, dtype, gamma, w_t, gbs, H, H_u, V, k, eps, flags, ps,
+                                   params, ncols, logits, vals, idx, tokens, L, ws,
+                                   (hipStream_t)stream));
+}
+
+TAIL_API int tail_forward_noalloc(const void* hidden, int dtype, const float* gamma,
+                                  const uint16_t* w_t, int gbs, int H, int H_u, int V, int k,
+                                  float eps, unsigned flags, const float* params, int ncols,
+                                  float* logits, float* vals, int32_t* idx, int32_t* tokens,
+                                  void* stream) {
+  int ps;
+  FwdLayout L;
+  if (int s = check_forward(hidden, dtype, gamma, w_t, gbs, H, H_u, V, k, eps, flags, params, ncols,
+                            logits, vals, idx, tokens, &ps, &L))
+    return s;
+  if (L.total > kScratchBytes) return TAIL_ERR_SCRATCH_LIMIT;
+  void* ws = scratch_address();
+  if (!ws) return TAIL_ERR_HIP;
+  return hip_status(forward_launch(hidden, dtype, gamma, w_t, gbs, H, H_u, V, k, eps, flags, ps,
+                                   params, ncols, logits, vals, idx, tokens, L, ws,
+                                   (hipStream_t)stream));
 }

@@ -51,6 +51,7 @@ extern "C" {
 #define TAIL_ERR_UNSUPPORTED 2 /* valid, but outside what the library implements */
 #define TAIL_ERR_WORKSPACE 3   /* workspace missing, misaligned or too small */
 #define TAIL_ERR_HIP 4         /* the HIP runtime rejected a launch */
+#define TAIL_ERR_SCRATCH_LIMIT 5 /* tail_forward_noalloc: more than TAIL_SCRATCH_BYTES needed */
 
 /* storage dtype of hidden_states ("hidden_states": fp32, fp16 or bf16) */
 #define TAIL_F32 0
@@ -244,6 +245,30 @@ int tail_forward(const void* hidden, int dtype, const float* gamma, const uint16
                  int H, int H_u, int V, int k, float eps, unsigned flags, const float* params,
                  int ncols, float* logits, float* vals, int32_t* idx, int32_t* tokens, void* ws,
                  size_t ws_bytes, void* stream);
+
+/*
+ * tail_forward_noalloc -- tail_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments and outputs without `ws`/`ws_bytes`.
+ * The workspace is a static array of TAIL_SCRATCH_BYTES inside the library,
+ * one per device, held from the library's first use on that device until
+ * the process ends; the call allocates and frees nothing.
+ *   - A call whose workspace (tail_workspace_size(...) bounds it) exceeds
+ *     TAIL_SCRATCH_BYTES returns TAIL_ERR_SCRATCH_LIMIT and enqueues nothing.
+ *     With the logits not emitted the workspace holds them, so at H = 2880
+ *     and V = 201088 the limit admits up to 79 rows; with TAIL_EMIT_LOGITS
+ *     (the logits in the caller's buffer) up to 1882.
+ *   - Every call on a device uses that device's one array: calls that may run
+ *     at the same time on one device (different streams, or threads without
+ *     ordering) race on it and must not overlap.  Nothing in it has to start
+ *     cleared: every call writes what it reads.
+ *   - TAIL_ERR_HIP if the array's device address cannot be obtained.
+ */
+#define TAIL_SCRATCH_BYTES (64u << 20)
+int tail_forward_noalloc(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t,
+                         int gbs, int H, int H_u, int V, int k, float eps, unsigned flags,
+                         const float* params, int ncols, float* logits, float* vals, int32_t* idx,
+                         int32_t* tokens, void* stream);
 
 /*
  * Workspace bytes needed by tail_forward, tail_rmsnorm_lm_head, tail_lm_head
