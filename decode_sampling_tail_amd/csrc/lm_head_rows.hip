@@ -61,43 +61,18 @@
 //
 // Determinism: every output element is one fixed sequence of MFMAs (K-steps
 // in order, terms in order), the same for every column and row.
-#include "tail_internal.h"
+#include "lds_copy.h"
 
 namespace tail {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-
-template <int N>
-__device__ inline void wait_vm() {
-  // vmcnt field split over bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Wait until at most PER * n of this wave's vector memory operations are
-// outstanding (0 <= n <= N, wave-uniform).
-template <int PER, int N>
-__device__ inline void wait_copies(int n) {
-  if constexpr (N <= 0) {
-    wait_vm<0>();
-  } else {
-    if (n >= N) wait_vm<PER * N>();
-    else wait_copies<PER, N - 1>(n);
-  }
-}
+using namespace mfma32;
 
 template <int NT, int MB, int NSW, int NSA>
 struct RCfg {
   static constexpr int NB = 2;                           // 32-row tiles per wave
   static constexpr int RT = 4 * NB;                      // row tiles per chunk (256 rows)
-  static constexpr int WPITCH = MB * 64 + ((64 - (MB * 64) % 256) + 256) % 256;
+  static constexpr int WPITCH = weight_pitch(MB);
   static constexpr int WCH = WPITCH / 16;                // 16-byte chunks per weight row
   static constexpr int WSTAGE = 16 * WPITCH;
   static constexpr int WCOP = WSTAGE / 1024;             // weight copies per step
@@ -113,58 +88,10 @@ struct RCfg {
                 "tile");
 };
 
-// Shared geometry of one call: the tiles of workgroup wg.
-struct RowsGeom {
-  int P, wg, nblk, tbase, textra, ntl, nks, total;
-  __device__ __forceinline__ RowsGeom(int V, int Kp, int npass) {
-    P = gridDim.x;
-    wg = blockIdx.x;
-    nblk = (V + 31) / 32;
-    const int ntiles = P * npass;
-    tbase = nblk / ntiles;
-    textra = nblk % ntiles;
-    // tiles j = 0 .. ntl - 1 are tiles j P + wg (widths do not grow with the
-    // tile index, so the non-empty ones come first)
-    ntl = 0;
-    while (ntl < npass && tbase + ((ntl * P + wg) < textra ? 1 : 0) > 0) ++ntl;
-    nks = Kp / 16;
-    total = ntl * nks;
-  }
-  __device__ __forceinline__ void tile(int j, int& start, int& width) const {
-    const int t = j * P + wg;
-    width = tbase + (t < textra ? 1 : 0);
-    start = t * tbase + (t < textra ? t : textra);
-  }
-};
-
-// lgkmcnt(0) only (vmcnt and expcnt left at their maximum)
-__device__ inline void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-__device__ inline void step_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// One direct copy of 16 bytes per lane from global memory into LDS at
-// lds_addr + 16 lane (lds_addr wave-uniform).  The copy takes its LDS address
-// from m0, which the statement sets itself; no other code of this kernel uses
-// m0 (it is a reserved register, so the clobber only documents the write).
-template <bool NONTEMPORAL>
-__device__ inline void copy_to_lds(const void* gptr, uint32_t lds_addr) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
-  if constexpr (NONTEMPORAL)
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-                 :: "v"(gptr), "s"(m0) : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(gptr), "s"(m0) : "memory", "m0");
-}
-
 // The copies of one wave: the weight (waves 0-3) or the activations (4-7).
 template <typename C, int NT, int NSW, int NSA>
 struct Copier {
-  const RowsGeom& G;
+  const TileGeom& G;
   uint32_t wring, aring;  // LDS byte addresses of the rings
   int wave, lane;
   const uint16_t* __restrict__ act;
@@ -246,18 +173,17 @@ __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, con
                                           int V, float* __restrict__ logits,
                                           uint32_t* __restrict__ gkey, int groups) {
   constexpr int NB = C::NB;
-  const int g = lane >> 4, s = lane & 15;
-  const int tr_off = (8 * (g >> 1) + (s >> 2)) * C::WPITCH + 32 * (g & 1) + 8 * (s & 3) + cb0 * 64;
+  const int tr_off = tr_lane_offset<C::WPITCH>(lane) + cb0 * 64;
   const int b_off = (rg * NB * 64 + lane) * 16;
   const int nks = cp.G.nks;
 
-  f32x16 acc[WC][NB];
+  f32x16 acc[NB][WC];
 #pragma unroll
-  for (int c = 0; c < WC; ++c)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int c = 0; c < WC; ++c)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[c][nb][e] = 0.0f;
+      for (int e = 0; e < 16; ++e) acc[nb][c][e] = 0.0f;
 
   bf16x8 bop[NB][NT], aop[WC];
   auto read = [&](int q) {
@@ -269,13 +195,7 @@ __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, con
       for (int t = 0; t < NT; ++t)
         bop[nb][t] = *reinterpret_cast<const lds_bf16x8*>(ast + (t * C::RT + nb) * 1024);
 #pragma unroll
-    for (int c = 0; c < WC; ++c) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(wst + c * 64));
-      const s16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(wst + c * 64 + 4 * C::WPITCH));
-      const s16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      aop[c] = __builtin_bit_cast(bf16x8, av);
-    }
+    for (int c = 0; c < WC; ++c) aop[c] = weight_operand<C::WPITCH>(wst + c * 64);
   };
   auto mma = [&]() {
 #pragma unroll
@@ -284,7 +204,7 @@ __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, con
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          acc[c][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[c], bop[nb][t], acc[c][nb], 0, 0, 0);
+          acc[nb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[c], bop[nb][t], acc[nb][c], 0, 0, 0);
   };
 
   for (int ks = 0; ks < nks; ++ks) {
@@ -302,38 +222,10 @@ __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, con
   if constexpr (LAG) mma();
 
   // epilogue: scaled logits, key-group maxima
-  const int nblk = cp.G.nblk;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int b = b0 + (rg * NB + nb) * 32 + (lane & 31);
-    const bool row_ok = b < gbs;
-    uint32_t prev = 0;  // maximum of the previous block
-#pragma unroll
-    for (int c = 0; c < WC; ++c) {
-      const int blk = blk0 + c;
-      uint32_t mx = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = blk * 32 + 8 * i + 4 * (lane >> 5);
-        const float4 o = make_float4(acc[c][nb][4 * i] * scale[nb], acc[c][nb][4 * i + 1] * scale[nb],
-                                     acc[c][nb][4 * i + 2] * scale[nb], acc[c][nb][4 * i + 3] * scale[nb]);
-        if (row_ok && v < V) {
-          *reinterpret_cast<float4*>(logits + size_t(b) * V + v) = o;
-          mx = max(mx, max(max(float_key(o.x), float_key(o.y)), max(float_key(o.z), float_key(o.w))));
-        }
-      }
-      mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
-      if (gkey && row_ok && lane < 32) {
-        uint32_t* dst = gkey + size_t(b) * groups + blk / 2;
-        const bool even = (blk & 1) == 0;
-        // a one-block last group has no partner
-        const bool partner_here = even ? (c + 1 < WC || blk + 1 >= nblk) : (c > 0);
-        if (!partner_here) atomicMax(dst, mx);  // the group straddles two waves
-        else if (!even) *dst = max(prev, mx);   // both blocks here: one store
-        else if (blk + 1 >= nblk) *dst = mx;
-      }
-      prev = mx;
-    }
+    store_tile<WC>(acc[nb], scale[nb], b, b < gbs, blk0, cp.G.nblk, lane, V, logits, gkey, groups);
   }
   (void)tstart;
   (void)twidth;
@@ -349,7 +241,7 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
   __shared__ __align__(1024) unsigned char smem[C::LDS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const RowsGeom G(V, Kp, npass);
+  const TileGeom G(V, Kp, npass);
   if (G.total == 0) return;  // the whole workgroup
   lds_u8* const wring = (lds_u8*)smem;
   lds_u8* const aring = wring + NSW * C::WSTAGE;

@@ -148,23 +148,48 @@ def test_lm_head_duplicate_columns_and_batch_invariance(big, H):
 @pytest.mark.parametrize("gbs,H,V", [(224, 256, 196928), (193, 200, 196928), (150, 200, 196928),
                                      (129, 64, 16448), (250, 64, 16448), (200, 96, 65600)])
 def test_lm_head_persistent_uneven_groups(page, gbs, H, V):
-    """Above 128 rows, on a vocabulary whose 64-column groups do not divide
-    over the persistent kernel's workgroups (the groups past the even split
-    go out as leftover items of one region x one row group with two terms,
-    as a partial extra sub-tile with one), the logits meet the parity bar
-    and columns duplicated between the whole sub-tiles and the leftover ones
-    give bitwise equal logits (every element takes its full K in order).
-    193 rows leave the last row group one row; with one term (the two-term
-    path runs up to 192 rows in 128-row chunks on the per-tile kernel) 150
-    and 129 rows leave one row group empty and one partly filled; K = 200
-    pads to 256 with clamped weight rows; K = 64 gives a single item step.  Vocabularies: 3077 groups (5 left over on 256 workgroups, one
-    partial region), 257 (one left over) and 1025."""
+    """Above 128 rows (the 32x32x16 large-batch kernel: one workgroup per CU,
+    the vocabulary's 32-column blocks cut into tiles of at most 9 blocks that
+    the workgroups take in interleaved passes), on vocabularies whose blocks
+    do not divide evenly over the tiles, the logits meet the parity bar and
+    columns duplicated far apart give bitwise-equal logits (every element
+    takes its full K in order).  196928 columns: 6154 blocks in 3 passes of
+    256 tiles, 10 of 9 blocks and 758 of 8; 16448: 514 blocks, one pass, 2
+    tiles of 3 and 254 of 2 (the second half of a 2-block tile is one
+    block); 65600: 2050 blocks, 2 tiles of 9 and 254 of 8.  193 rows leave
+    the last 32-row tile one row; 150 and 129 leave rows padding; K = 200
+    pads to 256 with clamped weight rows; K = 64 gives four K-steps."""
     rng = np.random.default_rng(11 + page + gbs)
     w = bf16_bits(rng.standard_normal((H, V)) * 0.05)
     groups = V // 64
     cut = groups // 256 * 256 * 64  # columns before the leftover on 256 workgroups
     src = rng.choice(cut, 48, replace=False)
     dup = cut + rng.choice(V - cut, 48, replace=False)
+    w[:, dup] = w[:, src]
+    y = rng.standard_normal((gbs, H)).astype(np.float32)
+    L = np_(dst.lm_head(torch.from_numpy(y).cuda(), gpu_bf16(w), page=page))
+    assert np.array_equal(L[:, src], L[:, dup])
+    yr = oracle.bf16_round(y) if page else y.astype(np.float64)
+    ref = oracle.logits(np.asarray(yr, np.float64), w, np.zeros(H, bool))
+    fails, rel, mx = check_logits(L, ref)
+    assert not fails, fails
+
+
+@pytest.mark.parametrize("page", [False, True])
+@pytest.mark.parametrize("gbs,H,V", [(4, 200, 131080), (32, 64, 262152), (33, 96, 196928),
+                                     (64, 200, 131080), (40, 64, 130568)])
+def test_lm_head_wide_vocab_small_batch(page, gbs, H, V):
+    """4 to 64 rows over vocabularies of more than 130560 columns (the
+    matrix-core kernel's 512-column tiles fill the chip, so K is not split):
+    the logits meet the parity bar and columns duplicated far apart give
+    bitwise-equal logits.  Vocabularies: a last tile of 8 columns (131080),
+    512 tiles (262152), last tiles of 320 and 8 columns (196928, 130568);
+    batches of one to four 16-row tiles, 33 and 40 leaving the last mostly
+    padding; K = 200 and 96 pad to 256 and 128 with clamped rows."""
+    rng = np.random.default_rng(17 + page + gbs + V)
+    w = bf16_bits(rng.standard_normal((H, V)) * 0.05)
+    src = rng.choice(V // 2, 64, replace=False)
+    dup = V // 2 + rng.choice(V - V // 2, 64, replace=False)
     w[:, dup] = w[:, src]
     y = rng.standard_normal((gbs, H)).astype(np.float32)
     L = np_(dst.lm_head(torch.from_numpy(y).cuda(), gpu_bf16(w), page=page))
