@@ -46,8 +46,6 @@
 // (given y); the products with the bf16 weights are then exact in fp32.
 #include "tail_internal.h"
 
-#include <hip/hip_fp16.h>
-
 namespace tail {
 namespace {
 
@@ -63,24 +61,11 @@ constexpr int kPrologueBurst = NB <= 4 ? 16 : 8;
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// A hidden element's raw bits (the fp32 pattern, or the 16-bit pattern
-// zero-extended), widened by widen_bits once the whole burst is issued.  The
-// prologues load every slot of a burst unconditionally, slots past the range
-// from a clamped valid lane, and zero those slots where the values are used:
-// a load inside a branch that widened its value (or that the compiler
+// The prologues load every slot of a burst unconditionally, slots past the
+// range from a clamped valid lane, and zero those slots where the values are
+// used: a load inside a branch that widened its value (or that the compiler
 // widened there) had to complete before the branch closed, one memory
 // latency per element.
-template <int DT>
-__device__ inline uint32_t load_bits(const void* p, size_t i) {
-  if constexpr (DT == 0) return __float_as_uint(static_cast<const float*>(p)[i]);
-  else return static_cast<const uint16_t*>(p)[i];
-}
-template <int DT>
-__device__ inline float widen_bits(uint32_t b) {
-  if constexpr (DT == 0) return __uint_as_float(b);
-  else if constexpr (DT == 1) return __half2float(__ushort_as_half(uint16_t(b)));
-  else return __uint_as_float(b << 16);
-}
 
 // butterfly sums over the 64 lanes of NB independent values at once: every
 // step exchanges all NB values before it waits, so the NB reductions share

@@ -13,32 +13,12 @@
 // batch.  Bytes per row: H * (dtype bytes + 4 gamma + 4 output).
 #include "tail_internal.h"
 
-#include <hip/hip_fp16.h>
-
 namespace tail {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPer = 16;  // lanes per thread per burst
 constexpr int kBurst = kThreads * kPer;
-
-// A hidden element's raw bits (the fp32 pattern, or the 16-bit pattern
-// zero-extended) and their widening.  Bursts load every slot
-// unconditionally (slots past the row from a clamped valid index) and zero
-// the out-of-range slots after widening: a load inside a branch that widened
-// its value (or that the compiler widened there) had to complete before the
-// branch closed, one memory latency per element.
-template <int DT>
-__device__ inline uint32_t load_bits(const void* p, size_t i) {
-  if constexpr (DT == 0) return __float_as_uint(static_cast<const float*>(p)[i]);
-  else return static_cast<const uint16_t*>(p)[i];
-}
-template <int DT>
-__device__ inline float widen_bits(uint32_t b) {
-  if constexpr (DT == 0) return __uint_as_float(b);
-  else if constexpr (DT == 1) return __half2float(__ushort_as_half(uint16_t(b)));
-  else return __uint_as_float(b << 16);
-}
 
 __device__ inline double wave_sum(double v) {
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -47,6 +27,10 @@ __device__ inline double wave_sum(double v) {
 
 __device__ inline bool is_pad(int h, int pad_s) { return pad_s && (h % pad_s == pad_s - 1); }
 
+// Bursts load every slot unconditionally (slots past the row from a clamped
+// valid index) and zero the out-of-range slots after widening: a load inside
+// a branch that widened its value (or that the compiler widened there) had
+// to complete before the branch closed, one memory latency per element.
 template <int DT>
 __device__ inline void load_burst(const void* hidden, size_t base, int h0, int H, int pad_s, int tid,
                                   float (&x)[kPer]) {

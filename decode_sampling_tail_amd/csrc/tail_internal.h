@@ -2,6 +2,7 @@
 // units of the decode-tail library (gfx950 only).  Not part of the ABI.
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -71,6 +72,21 @@ T per_device(std::once_flag (&once)[kMaxDevices], T (&value)[kMaxDevices], F&& i
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return init(dev);
   std::call_once(once[dev], [&] { value[dev] = init(dev); });
   return value[dev];
+}
+
+// A hidden element's raw bits (the fp32 pattern, or the 16-bit pattern
+// zero-extended) from element i of a row-major hidden array of dtype DT
+// (0 fp32, 1 fp16, 2 bf16), and their exact widening to fp32.
+template <int DT>
+__device__ inline uint32_t load_bits(const void* p, size_t i) {
+  if constexpr (DT == 0) return __float_as_uint(static_cast<const float*>(p)[i]);
+  else return static_cast<const uint16_t*>(p)[i];
+}
+template <int DT>
+__device__ inline float widen_bits(uint32_t b) {
+  if constexpr (DT == 0) return __uint_as_float(b);
+  else if constexpr (DT == 1) return __half2float(__ushort_as_half(uint16_t(b)));
+  else return __uint_as_float(b << 16);
 }
 
 // Order-preserving key of a float: larger float <=> larger unsigned key.
