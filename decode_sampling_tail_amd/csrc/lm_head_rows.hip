@@ -20,7 +20,10 @@
 //
 // A workgroup has 8 waves, two per SIMD.  Wave w owns rows 64 (w % 4) ..
 // + 63 of the chunk and the first (w < 4) or second half of the tile's
-// blocks, in accumulators of 32 x 32.  Per K-step of 16 hidden lanes the
+// blocks, in accumulators of 32 x 32.  A wave whose rows are all padding
+// (a last chunk of fewer than 256 rows) skips its reads and MFMAs and only
+// takes part in the copies and barriers; one with one real 32-row tile
+// multiplies only that one.  Per K-step of 16 hidden lanes the
 // tile's weight [16 x 32 W] goes to an LDS ring of NSW stages, NSW - 1 steps
 // ahead, and the step's activation fragments (256 rows x NT terms) to a ring
 // of NSA stages, NSA - 1 steps ahead, by direct global-to-LDS copies: waves
@@ -166,7 +169,7 @@ struct Copier {
 // One wave's part of one tile (steps q0 .. q0 + nks - 1): WC blocks starting
 // at block cb0 of the tile, rows 64 rg .. 64 rg + 63.  LAG: the wave runs each
 // step's MFMAs after the next barrier (see above).
-template <typename C, typename CP, int NT, int NSW, int NSA, int WC, bool LAG>
+template <typename C, typename CP, int NT, int NSW, int NSA, int WC, int NV, bool LAG>
 __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, const lds_u8* aring,
                                           int rg, int lane, int q0, int blk0, int cb0, int tstart,
                                           int twidth, const float (&scale)[2], int b0, int gbs,
@@ -177,20 +180,20 @@ __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, con
   const int b_off = (rg * NB * 64 + lane) * 16;
   const int nks = cp.G.nks;
 
-  f32x16 acc[NB][WC];
+  f32x16 acc[NV][WC];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int nb = 0; nb < NV; ++nb)
 #pragma unroll
     for (int c = 0; c < WC; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[nb][c][e] = 0.0f;
 
-  bf16x8 bop[NB][NT], aop[WC];
+  bf16x8 bop[NV][NT], aop[WC];
   auto read = [&](int q) {
     const lds_u8* wst = wring + (q % NSW) * C::WSTAGE + tr_off;
     const lds_u8* ast = aring + (q % NSA) * C::ASTAGE + b_off;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NV; ++nb)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         bop[nb][t] = *reinterpret_cast<const lds_bf16x8*>(ast + (t * C::RT + nb) * 1024);
@@ -203,7 +206,7 @@ __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, con
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NV; ++nb)
           acc[nb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[c], bop[nb][t], acc[nb][c], 0, 0, 0);
   };
 
@@ -223,7 +226,7 @@ __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, con
 
   // epilogue: scaled logits, key-group maxima
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  for (int nb = 0; nb < NV; ++nb) {
     const int b = b0 + (rg * NB + nb) * 32 + (lane & 31);
     store_tile<WC>(acc[nb], scale[nb], b, b < gbs, blk0, cp.G.nblk, lane, V, logits, gkey, groups);
   }
@@ -250,6 +253,9 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
               K, pad_s, pdiv, b0};
 
   const int rg = wave & 3, half = wave >> 2;
+  // this wave's 32-row tiles that hold rows of the batch (the others are
+  // padding: their reads and MFMAs are skipped)
+  const int nv = min(max((gbs - b0 + 31) / 32 - 2 * rg, 0), 2);
   float scale[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -266,21 +272,30 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
     const int w0 = (width + 1) / 2;
     const int cb0 = half ? w0 : 0, wc = half ? width - w0 : w0;
     const int q0 = j * G.nks;
+#define TAIL_ROWS_PART_NV(WW, NVV)                                                             \
+  if (half)                                                                                     \
+    tile_part<C, CP, NT, NSW, NSA, WW, NVV, true>(cp, wring, aring, rg, lane, q0, start + cb0,  \
+                                                  cb0, start, width, scale, b0, gbs, V, logits, \
+                                                  gkey, groups);                                \
+  else                                                                                          \
+    tile_part<C, CP, NT, NSW, NSA, WW, NVV, false>(cp, wring, aring, rg, lane, q0, start + cb0, \
+                                                   cb0, start, width, scale, b0, gbs, V, logits,\
+                                                   gkey, groups);
 #define TAIL_ROWS_PART(WW)                                                                       \
   case WW:                                                                                       \
     if constexpr (WW <= C::HB) {                                                                 \
-      if (half)                                                                                  \
-        tile_part<C, CP, NT, NSW, NSA, WW, true>(cp, wring, aring, rg, lane, q0, start + cb0, cb0, \
-                                                 start, width, scale, b0, gbs, V, logits, gkey,  \
-                                                 groups);                                        \
-      else                                                                                       \
-        tile_part<C, CP, NT, NSW, NSA, WW, false>(cp, wring, aring, rg, lane, q0, start + cb0,   \
-                                                  cb0, start, width, scale, b0, gbs, V, logits,  \
-                                                  gkey, groups);                                 \
+      if (nv == 2) {                                                                             \
+        TAIL_ROWS_PART_NV(WW, 2)                                                                 \
+      } else {                                                                                   \
+        TAIL_ROWS_PART_NV(WW, 1)                                                                 \
+      }                                                                                          \
     }                                                                                            \
     break;
-    switch (wc) {
-      case 0:  // a one-block tile leaves the second half empty: barriers only
+    // a one-block tile leaves the second half empty, and a chunk of fewer
+    // than 256 rows leaves the waves of its all-padding 32-row tiles idle:
+    // barriers (and their share of the copies) only
+    switch (nv == 0 ? 0 : wc) {
+      case 0:
         for (int ks = 0; ks < G.nks; ++ks) {
           cp.step(q0 + ks);
           cp.refill(q0 + ks);
@@ -289,6 +304,7 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
       TAIL_ROWS_PART(1) TAIL_ROWS_PART(2) TAIL_ROWS_PART(3) TAIL_ROWS_PART(4) TAIL_ROWS_PART(5)
       default: break;
     }
+#undef TAIL_ROWS_PART_NV
 #undef TAIL_ROWS_PART
   }
 }
