@@ -17,7 +17,8 @@
  *    (compute-unit count, kernel occupancy, the raised LDS limit), each
  *    filled once, thread-safely, the first time a call runs on that device
  *    and never changed afterwards; no call's result depends on them beyond
- *    the launch shape.
+ *    the launch shape.  tail_forward_noalloc alone also uses a static
+ *    scratch array in each device's memory (see its declaration).
  *  - Arrays are C-contiguous (row-major) with the shapes given.
  *  - Every call validates its arguments on the host BEFORE any HIP call and
  *    returns a status code; on an error nothing is enqueued and no output is
