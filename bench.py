@@ -288,11 +288,12 @@ def bench_workload(cid, args, torch, np):
 
 
 def rows_padded(gbs):
-    """Rows the matrix-core kernels compute: 16-row tiles up to 128 rows,
-    then 256-row chunks of 32-row tiles."""
-    if gbs <= 128:
+    """Rows the matrix-core kernels multiply at the full vocabulary: 16-row
+    tiles up to 64 rows, then 32-row tiles (the large-batch kernel skips the
+    MFMAs of its all-padding tiles)."""
+    if gbs <= 64:
         return (gbs + 15) // 16 * 16
-    return (gbs + 255) // 256 * 256
+    return (gbs + 31) // 32 * 32
 
 
 SHARDS = 8  # vocabulary shards of the multi-GPU design; one shard's shape is timed here

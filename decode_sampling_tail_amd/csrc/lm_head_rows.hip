@@ -1,5 +1,6 @@
-// lm_head contraction for batches of more than 128 rows, on the bf16 matrix
-// cores with v_mfma_f32_32x32x16_bf16 (GPT-OSS tail API page, parameter
+// lm_head contraction for batches of more than 64 rows (from 65 to 128 only
+// over a vocabulary wide enough to fill the chip without splitting K), on
+// the bf16 matrix cores with v_mfma_f32_32x32x16_bf16 (GPT-OSS tail API page, parameter
 // "lm_head_weight_t": [H, V] bf16, already transposed and C-contiguous).
 //
 // logits[b, v] = row_scale[b] * sum_h (sum_t A_t[b, h]) * W[h, v]
@@ -10,22 +11,27 @@
 // ready B-operand fragments: one 1 KB fragment per (16-lane K block, term,
 // 32-row tile), lane 32 h + n holding row n at K lanes 8 h .. 8 h + 7.
 //
-// One call covers a chunk of 256 batch rows for the whole vocabulary, with
-// one persistent workgroup per CU.  The vocabulary is cut into 32-column
+// One launch covers a chunk of 32 RT batch rows for the whole vocabulary,
+// with one persistent workgroup per CU: RT = 8 (256-row chunks) with tiles
+// of up to MB = 9 blocks above 128 rows, RT = 4 (one 128-row chunk) with
+// tiles of up to 13 blocks from 65 to 128 rows (one 32-row tile per wave
+// leaves the accumulators for the wider tile: 2 passes instead of 3 over
+// the activations).  The vocabulary is cut into 32-column
 // blocks and the blocks into npass * P tiles of equal width (to within one
 // block, at most MB blocks); workgroup w takes tiles w, w + P, w + 2P, ...,
 // so at any time the P workgroups read one contiguous column range of every
 // weight row (whole DRAM pages together: measured 6.9 TB/s for the weight
 // stream alone against 5.3 TB/s with contiguous per-workgroup ranges).
 //
-// A workgroup has 8 waves, two per SIMD.  Wave w owns rows 64 (w % 4) ..
-// + 63 of the chunk and the first (w < 4) or second half of the tile's
-// blocks, in accumulators of 32 x 32.  A wave whose rows are all padding
-// (a last chunk of fewer than 256 rows) skips its reads and MFMAs and only
+// A workgroup has 8 waves, two per SIMD.  Wave w owns NB = RT / 4 32-row
+// tiles of the chunk (rows 32 NB (w % 4) .. + 32 NB - 1) and the first
+// (w < 4) or second half of the tile's blocks, in accumulators of 32 x 32.
+// A wave whose rows are all padding (a short last chunk) skips its reads
+// and MFMAs and only
 // takes part in the copies and barriers; one with one real 32-row tile
 // multiplies only that one.  Per K-step of 16 hidden lanes the
 // tile's weight [16 x 32 W] goes to an LDS ring of NSW stages, NSW - 1 steps
-// ahead, and the step's activation fragments (256 rows x NT terms) to a ring
+// ahead, and the step's activation fragments (RT tiles x NT terms) to a ring
 // of NSA stages, NSA - 1 steps ahead, by direct global-to-LDS copies: waves
 // 0-3 copy the weight, waves 4-7 the activations, so each wave waits only on
 // one stream (vector memory operations complete in issue order per wave: one
@@ -71,10 +77,11 @@ namespace {
 
 using namespace mfma32;
 
-template <int NT, int MB, int NSW, int NSA>
+template <int NT, int NBT, int MB, int NSW, int NSA>
 struct RCfg {
-  static constexpr int NB = 2;                           // 32-row tiles per wave
-  static constexpr int RT = 4 * NB;                      // row tiles per chunk (256 rows)
+  static constexpr int NB = NBT;                         // 32-row tiles per wave (1 or 2)
+  static constexpr int RT = 4 * NB;                      // row tiles per chunk (128 or 256 rows)
+  static constexpr int CHUNK = 32 * RT;
   static constexpr int WPITCH = weight_pitch(MB);
   static constexpr int WCH = WPITCH / 16;                // 16-byte chunks per weight row
   static constexpr int WSTAGE = 16 * WPITCH;
@@ -172,7 +179,7 @@ struct Copier {
 template <typename C, typename CP, int NT, int NSW, int NSA, int WC, int NV, bool LAG>
 __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, const lds_u8* aring,
                                           int rg, int lane, int q0, int blk0, int cb0, int tstart,
-                                          int twidth, const float (&scale)[2], int b0, int gbs,
+                                          int twidth, const float (&scale)[C::NB], int b0, int gbs,
                                           int V, float* __restrict__ logits,
                                           uint32_t* __restrict__ gkey, int groups) {
   constexpr int NB = C::NB;
@@ -234,12 +241,12 @@ __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, con
   (void)twidth;
 }
 
-template <int NT, int MB, int NSW, int NSA>
+template <int NT, int NB, int MB, int NSW, int NSA>
 __global__ __launch_bounds__(512, 1) void rows_kernel(
     const uint16_t* __restrict__ act, int nrt, int Kp, const uint16_t* __restrict__ w, int V, int K,
     int pad_s, FastDiv pdiv, const float* __restrict__ row_scale, int gbs, int b0,
     float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups, int npass) {
-  using C = RCfg<NT, MB, NSW, NSA>;
+  using C = RCfg<NT, NB, MB, NSW, NSA>;
   using CP = Copier<C, NT, NSW, NSA>;
   __shared__ __align__(1024) unsigned char smem[C::LDS];
   const int lane = threadIdx.x & 63;
@@ -255,11 +262,11 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
   const int rg = wave & 3, half = wave >> 2;
   // this wave's 32-row tiles that hold rows of the batch (the others are
   // padding: their reads and MFMAs are skipped)
-  const int nv = min(max((gbs - b0 + 31) / 32 - 2 * rg, 0), 2);
-  float scale[2];
+  const int nv = min(max((gbs - b0 + 31) / 32 - NB * rg, 0), NB);
+  float scale[NB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int b = b0 + (rg * 2 + nb) * 32 + (lane & 31);
+  for (int nb = 0; nb < NB; ++nb) {
+    const int b = b0 + (rg * NB + nb) * 32 + (lane & 31);
     scale[nb] = (b < gbs && row_scale) ? row_scale[b] : 1.0f;
   }
   // the scales have arrived before the first copy is issued
@@ -284,15 +291,19 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
 #define TAIL_ROWS_PART(WW)                                                                       \
   case WW:                                                                                       \
     if constexpr (WW <= C::HB) {                                                                 \
-      if (nv == 2) {                                                                             \
-        TAIL_ROWS_PART_NV(WW, 2)                                                                 \
+      if constexpr (NB == 2) {                                                                   \
+        if (nv == 2) {                                                                           \
+          TAIL_ROWS_PART_NV(WW, 2)                                                               \
+        } else {                                                                                 \
+          TAIL_ROWS_PART_NV(WW, 1)                                                               \
+        }                                                                                        \
       } else {                                                                                   \
         TAIL_ROWS_PART_NV(WW, 1)                                                                 \
       }                                                                                          \
     }                                                                                            \
     break;
-    // a one-block tile leaves the second half empty, and a chunk of fewer
-    // than 256 rows leaves the waves of its all-padding 32-row tiles idle:
+    // a one-block tile leaves the second half empty, and a short last chunk
+    // leaves the waves of its all-padding 32-row tiles idle:
     // barriers (and their share of the copies) only
     switch (nv == 0 ? 0 : wc) {
       case 0:
@@ -302,6 +313,7 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
         }
         break;
       TAIL_ROWS_PART(1) TAIL_ROWS_PART(2) TAIL_ROWS_PART(3) TAIL_ROWS_PART(4) TAIL_ROWS_PART(5)
+      TAIL_ROWS_PART(6) TAIL_ROWS_PART(7)
       default: break;
     }
 #undef TAIL_ROWS_PART_NV
@@ -309,11 +321,11 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
   }
 }
 
-template <int NT, int MB, int NSW, int NSA>
+template <int NT, int NB, int MB, int NSW, int NSA>
 hipError_t launch_rows_cfg(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V,
-                           int K, int pad_s, const float* row_scale, int gbs, int b0,
-                           float* logits, uint32_t* gkey, hipStream_t st) {
-  auto kern = rows_kernel<NT, MB, NSW, NSA>;
+                           int K, int pad_s, const float* row_scale, int gbs, float* logits,
+                           uint32_t* gkey, hipStream_t st) {
+  auto kern = rows_kernel<NT, NB, MB, NSW, NSA>;
   static std::once_flag once[kMaxDevices];
   static int cus_cache[kMaxDevices];
   const int cus = per_device(once, cus_cache, [&](int dev) {
@@ -327,9 +339,13 @@ hipError_t launch_rows_cfg(const uint16_t* act, int rows_pad, int Kp, const uint
   const int P = nblk < cus ? nblk : cus;
   const int npass = (nblk + P * MB - 1) / (P * MB);
   const int groups = (V + kFusedGroup - 1) / kFusedGroup;
-  hipLaunchKernelGGL(kern, dim3(P), dim3(512), 0, st, act, rows_pad / 32, Kp, w, V, K, pad_s, pdiv,
-                     row_scale, gbs, b0, logits, gkey, groups, npass);
-  return hipGetLastError();
+  for (int b0 = 0; b0 < gbs; b0 += RCfg<NT, NB, MB, NSW, NSA>::CHUNK) {
+    hipLaunchKernelGGL(kern, dim3(P), dim3(512), 0, st, act, rows_pad / 32, Kp, w, V, K, pad_s,
+                       pdiv, row_scale, gbs, b0, logits, gkey, groups, npass);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -337,19 +353,25 @@ hipError_t launch_rows_cfg(const uint16_t* act, int rows_pad, int Kp, const uint
 hipError_t launch_lm_head_rows(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,
                                int V, int K, int pad_s, const float* row_scale, int gbs,
                                float* logits, uint32_t* gkey, hipStream_t st) {
-  for (int b0 = 0; b0 < gbs; b0 += 256) {
-    hipError_t e;
+  // up to 128 rows: 128-row chunks of one 32-row tile per wave, whose
+  // accumulators leave room for 13-block tiles (2 passes for GPT-OSS);
+  // above: 256-row chunks of two tiles per wave and 9-block tiles (3 passes)
+  if (gbs <= 128) {
     if (nt == 2)
-      e = launch_rows_cfg<2, 9, 8, 4>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs, b0, logits,
-                                      gkey, st);
-    else if (nt == 1)
-      e = launch_rows_cfg<1, 9, 8, 6>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs, b0, logits,
-                                      gkey, st);
-    else
-      e = hipErrorInvalidValue;
-    if (e != hipSuccess) return e;
+      return launch_rows_cfg<2, 1, 13, 8, 4>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs,
+                                             logits, gkey, st);
+    if (nt == 1)
+      return launch_rows_cfg<1, 1, 13, 8, 6>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs,
+                                             logits, gkey, st);
+    return hipErrorInvalidValue;
   }
-  return hipSuccess;
+  if (nt == 2)
+    return launch_rows_cfg<2, 2, 9, 8, 4>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs, logits,
+                                          gkey, st);
+  if (nt == 1)
+    return launch_rows_cfg<1, 2, 9, 8, 6>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs, logits,
+                                          gkey, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tail

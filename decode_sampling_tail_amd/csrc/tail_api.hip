@@ -55,14 +55,15 @@ int check_k(int V, int k) {
 // Geometry of the matrix-core path's split activations: [nt][rows_pad][Kp] bf16
 // (nt = 1 in the page-precision mode).
 struct SplitGeom {
-  int K, Kp, rows_pad, nt;
+  int K, Kp, rows_pad, nt, layout;
   size_t bytes;
 };
-SplitGeom split_geom(int gbs, int H, int H_u, int pad_s, unsigned flags) {
+SplitGeom split_geom(int gbs, int H, int H_u, int pad_s, int V, unsigned flags) {
   SplitGeom g;
   g.K = pad_s ? H_u : H;
   g.Kp = (g.K + tail::kKStep - 1) / tail::kKStep * tail::kKStep;
-  const int rt = tail::mfma_row_tile(gbs);
+  g.layout = tail::mfma_layout(gbs, V, g.Kp);
+  const int rt = tail::mfma_row_tile(g.layout);
   g.rows_pad = (gbs + rt - 1) / rt * rt;
   g.nt = tail::mfma_terms(gbs, flags & TAIL_PAGE_PRECISION);
   g.bytes = gbs > tail::kGemvMaxBatch ? size_t(g.nt) * g.rows_pad * g.Kp * 2 : 0;
@@ -77,8 +78,8 @@ struct FwdLayout {
 size_t gemv_part(int gbs, int H, int H_u, int pad_s, int V) {
   const int K = pad_s ? H_u : H;
   if (gbs <= tail::kGemvMaxBatch) return tail::gemv_part_bytes(gbs, K, V);
-  if (tail::mfma_layout(gbs)) return 0;  // the large-batch kernel never splits K
   const int Kp = (K + tail::kKStep - 1) / tail::kKStep * tail::kKStep;
+  if (tail::mfma_layout(gbs, V, Kp)) return 0;  // the large-batch kernel never splits K
   return tail::mfma_part_bytes(gbs, Kp, V);
 }
 
@@ -92,7 +93,7 @@ FwdLayout forward_layout(int gbs, int H, int H_u, int pad_s, int V, int k, unsig
   L.r = off;
   off = align256(off + size_t(gbs) * 4);
   L.act = off;
-  off = align256(off + split_geom(gbs, H, H_u, pad_s, flags).bytes);
+  off = align256(off + split_geom(gbs, H, H_u, pad_s, V, flags).bytes);
   L.part = off;
   off = align256(off + gemv_part(gbs, H, H_u, pad_s, V));
   L.logits = off;
@@ -123,7 +124,7 @@ hipError_t norm_lm_head(const void* hidden, int dtype, const float* gamma, const
                         float* r, uint16_t* act, void* part, float* logits, uint32_t* gkey,
                         hipStream_t st) {
   const bool deferred = flags & TAIL_DEFERRED_RMS, page = flags & TAIL_PAGE_PRECISION;
-  const SplitGeom sg = split_geom(gbs, H, H_u, ps, flags);
+  const SplitGeom sg = split_geom(gbs, H, H_u, ps, V, flags);
   if (tail::gemv_fusable(gbs, sg.K))
     return tail::launch_norm_gemv(hidden, dtype, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, page,
                                   w_t, V, logits, r, gkey, part, st);
@@ -135,7 +136,7 @@ hipError_t norm_lm_head(const void* hidden, int dtype, const float* gamma, const
                                     logits, gkey, part, st);
     return e;
   }
-  const int layout = tail::mfma_layout(gbs);
+  const int layout = sg.layout;
   // the large-batch kernel combines straddling key groups into cleared entries
   uint32_t* gz = layout ? gkey : nullptr;
   e = tail::launch_split(hidden, dtype, true, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, sg.nt,
@@ -173,7 +174,7 @@ TAIL_API size_t tail_workspace_size(int gbs, int H, int H_u, int V, int k, unsig
   size_t tk = topk_ws_bytes(gbs, V, k);
   // tail_lm_head: the split-K partials, after the split activations on the
   // matrix-core path
-  const size_t lm = align256(split_geom(gbs, H, H_u, ps, flags).bytes) +
+  const size_t lm = align256(split_geom(gbs, H, H_u, ps, V, flags).bytes) +
                     align256(gemv_part(gbs, H, H_u, ps, V));
   size_t m = fwd > tk ? fwd : tk;
   return m > lm ? m : lm;
@@ -210,7 +211,7 @@ TAIL_API int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_
   if (!aligned(y, 4) || !aligned(w_t, 16) || !aligned(logits, 16) ||
       (row_scale && !aligned(row_scale, 4)))
     return TAIL_ERR_INVALID_ARG;
-  const SplitGeom sg = split_geom(gbs, H, H_u, ps, flags);
+  const SplitGeom sg = split_geom(gbs, H, H_u, ps, V, flags);
   hipStream_t st = (hipStream_t)stream;
   if (gbs <= tail::kGemvMaxBatch) {
     if (int s = check_ws(ws, ws_bytes, gemv_part(gbs, H, H_u, ps, V))) return s;
@@ -221,7 +222,7 @@ TAIL_API int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_
   // matrix-core path: the split activations, then the split-K partials
   if (int s = check_ws(ws, ws_bytes, align256(sg.bytes) + gemv_part(gbs, H, H_u, ps, V))) return s;
   uint16_t* act = (uint16_t*)ws;
-  const int layout = tail::mfma_layout(gbs);
+  const int layout = sg.layout;
   hipError_t e = tail::launch_split(y, TAIL_F32, false, nullptr, gbs, H, H_u, sg.K, ps, 0.0f, false,
                                     sg.nt, layout, sg.rows_pad, sg.Kp, act, nullptr, nullptr, 0, st);
   if (e == hipSuccess)

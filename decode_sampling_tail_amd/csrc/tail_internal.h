@@ -150,12 +150,19 @@ constexpr int kGemvMaxBatch = 3;
 constexpr int kKStep = 64;  // K granularity of the matrix-core path
 int mfma_terms(int gbs, bool page);  // bf16 terms per activation (1 in the page-precision mode)
 
-// Batches above this size run the lm_head on the 32x32x16 large-batch kernel
-// (lm_head_rows.hip), which reads its activations in fragment layout 1; the
-// others in layout 0 (lm_head_mfma.hip).
+// Batches of kRowsMinBatch rows and more run the lm_head on the 32x32x16
+// large-batch kernel (lm_head_rows.hip), and so do batches from
+// kRowsMidBatch rows over a vocabulary whose 512-column tiles fill the chip
+// (where the 16x16x32 kernel would not split K); they read their
+// activations in fragment layout 1, the others in layout 0
+// (lm_head_mfma.hip), which splits K for narrow vocabularies.
 constexpr int kRowsMinBatch = 129;
-inline int mfma_layout(int gbs) { return gbs >= kRowsMinBatch ? 1 : 0; }
-inline int mfma_row_tile(int gbs) { return mfma_layout(gbs) ? 32 : 16; }
+constexpr int kRowsMidBatch = 65;
+int mfma_ksplit(int V, int Kp);
+inline int mfma_layout(int gbs, int V, int Kp) {
+  return (gbs >= kRowsMinBatch || (gbs >= kRowsMidBatch && mfma_ksplit(V, Kp) == 1)) ? 1 : 0;
+}
+inline int mfma_row_tile(int layout) { return layout ? 32 : 16; }
 
 // Split (and, with norm, RMS-normalize) activations for the matrix-core path:
 // act holds nt * rows_pad * Kp bf16 bits over the K contraction lanes as 1 KB
@@ -170,13 +177,12 @@ hipError_t launch_split(const void* src, int dtype, bool norm, const float* gamm
 
 // Matrix-core lm_head; part_ws: mfma_part_bytes(gbs, Kp, V) bytes (256-byte
 // aligned) for the split-K partials of a narrow vocabulary.
-int mfma_ksplit(int V, int Kp);
 size_t mfma_part_bytes(int gbs, int Kp, int V);
 hipError_t launch_lm_head_mfma(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,
                                int V, int H_u, int pad_s, const float* row_scale, int gbs,
                                float* logits, uint32_t* gkey, void* part_ws, hipStream_t st);
 
-// The large-batch lm_head (gbs >= kRowsMinBatch): act in layout 1 with
+// The large-batch lm_head (layout 1 batches, see mfma_layout): act in layout 1 with
 // rows_pad a multiple of 32; gkey (may be NULL) must hold zeros where the
 // producer cleared it.
 hipError_t launch_lm_head_rows(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,

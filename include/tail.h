@@ -29,10 +29,13 @@
  *    neither on the column's position nor on the other rows of the batch, so
  *    duplicated weight columns give bitwise-equal logits.  The path depends
  *    on the batch size: weight streaming with fp32 FMAs up to 3 rows, the
- *    16x16x32 matrix-core kernel from 4 to 128 rows, the 32x32x16 kernel
- *    above; each sums in its own fixed order, so a row's logits may differ
- *    in the last bits when the batch crosses 3/4 or 128/129 rows (each path
- *    meets the same accuracy bar).
+ *    16x16x32 matrix-core kernel from 4 to 64 rows, the 32x32x16 kernel
+ *    above (from 65 to 128 rows only where the 16x16x32 kernel would not
+ *    split K: V above 130560 columns, or fewer than 512 padded K lanes;
+ *    otherwise it keeps those batches too, with K split); each sums in its
+ *    own fixed order, so a row's logits may differ in the last bits when the
+ *    batch crosses 3/4 or 64/65 rows (128/129 where K is split); each path
+ *    meets the same accuracy bar.
  *  - Calls on different streams may run concurrently as long as they do not
  *    share output or workspace memory.
  */

@@ -145,6 +145,41 @@ def test_lm_head_duplicate_columns_and_batch_invariance(big, H):
 
 
 @pytest.mark.parametrize("page", [False, True])
+def test_rows_across_path_boundaries(page):
+    """The lm_head path depends on the batch size (over a vocabulary wide
+    enough to need no split K: weight streaming up to 3 rows, 16x16x32
+    matrix cores from 4 to 64, the 32x32x16 large-batch kernel above), each
+    path with its own summation order, so the same rows in batches on both
+    sides of the 3/4 and 64/65 boundaries give logits that may differ in the
+    last bits but each meet the parity bar against the oracle, and differ
+    from one another by no more than twice the bar.  Within one path the
+    bytes do not depend on the batch: 2 rows inside 3, 4 inside 17 and 64,
+    and 65 inside 128, 129 and 200 (the large-batch kernel's 128-row and
+    256-row chunk shapes multiply in the same order)."""
+    rng = np.random.default_rng(23 + page)
+    H, V = 2880, 131080
+    w = bf16_bits(rng.standard_normal((H, V)) * 0.02)
+    y = rng.standard_normal((200, H)).astype(np.float32)
+    wt = gpu_bf16(w)
+    yt = torch.from_numpy(y).cuda()
+    L = {n: np_(dst.lm_head(yt[:n].contiguous(), wt, page=page))
+         for n in (2, 3, 4, 17, 64, 65, 128, 129, 200)}
+    yr = oracle.bf16_round(y[:3]) if page else y[:3].astype(np.float64)
+    ref = oracle.logits(np.asarray(yr, np.float64), w, np.zeros(H, bool))
+    for n in (3, 4, 64, 65, 128, 129):
+        fails, rel, mx = check_logits(L[n][:3], ref)
+        assert not fails, (n, fails)
+    for a, b in ((3, 4), (64, 65)):
+        d = L[a][:3].astype(np.float64) - L[b][:3]
+        rel = np.sqrt((d * d).sum(1) / (ref * ref).sum(1))
+        assert np.all(rel <= 2e-5) and np.abs(d).max() <= 4e-3, (a, b, rel.max())
+    same = lambda a, b: np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert same(L[2], L[3][:2])
+    assert same(L[4], L[17][:4]) and same(L[4], L[64][:4])
+    assert same(L[65], L[128][:65]) and same(L[65], L[129][:65]) and same(L[65], L[200][:65])
+
+
+@pytest.mark.parametrize("page", [False, True])
 @pytest.mark.parametrize("gbs,H,V", [(224, 256, 196928), (193, 200, 196928), (150, 200, 196928),
                                      (129, 64, 16448), (250, 64, 16448), (200, 96, 65600)])
 def test_lm_head_persistent_uneven_groups(page, gbs, H, V):
@@ -177,15 +212,20 @@ def test_lm_head_persistent_uneven_groups(page, gbs, H, V):
 
 @pytest.mark.parametrize("page", [False, True])
 @pytest.mark.parametrize("gbs,H,V", [(4, 200, 131080), (32, 64, 262152), (33, 96, 196928),
-                                     (64, 200, 131080), (40, 64, 130568)])
+                                     (64, 200, 131080), (40, 64, 130568), (65, 200, 131080),
+                                     (96, 64, 262152), (128, 96, 196928), (100, 2880, 201088)])
 def test_lm_head_wide_vocab_small_batch(page, gbs, H, V):
-    """4 to 64 rows over vocabularies of more than 130560 columns (the
-    matrix-core kernel's 512-column tiles fill the chip, so K is not split):
-    the logits meet the parity bar and columns duplicated far apart give
-    bitwise-equal logits.  Vocabularies: a last tile of 8 columns (131080),
-    512 tiles (262152), last tiles of 320 and 8 columns (196928, 130568);
-    batches of one to four 16-row tiles, 33 and 40 leaving the last mostly
-    padding; K = 200 and 96 pad to 256 and 128 with clamped rows."""
+    """4 to 128 rows over vocabularies of more than 130560 columns (the
+    16x16x32 kernel's 512-column tiles fill the chip, so K is not split; from
+    65 rows the large-batch kernel's 128-row shape runs): the logits meet the
+    parity bar and columns duplicated far apart give bitwise-equal logits.
+    Vocabularies: a last 16x16x32 tile of 8 columns (131080; for the
+    large-batch kernel 4097 blocks in 2 passes of 8 or 9), 512 tiles (262152;
+    3 passes of 10 or 11 blocks), last tiles of 320 and 8 columns (196928:
+    2 passes of 12 or 13 blocks; 130568); batches of one to four 16-row
+    tiles, 33 and 40 leaving the last mostly padding, 65 and 100 leaving the
+    large-batch kernel's last 32-row tile mostly padding; K = 200 and 96 pad
+    to 256 and 128 with clamped rows; GPT-OSS's shape at 100 rows."""
     rng = np.random.default_rng(17 + page + gbs + V)
     w = bf16_bits(rng.standard_normal((H, V)) * 0.05)
     src = rng.choice(V // 2, 64, replace=False)
