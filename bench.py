@@ -424,7 +424,7 @@ def main():
             frac=r["lm_head_mfma_alg_frac"], executed=r["lm_head_mfma_exec_tflops"],
             frac_executed=r["lm_head_mfma_frac"],
             traffic=counter_traffic(ROWS_COUNTERS, ROWS_SOURCES),
-            kernel="rows_kernel<2,9,8,4>: 32x32x16 matrix-core lm_head, gbs 256 (the time "
+            kernel="rows_kernel<2,13,8,3,1>: 32x32x16 matrix-core lm_head, gbs 256 (the time "
                    "includes its RMSNorm/bf16-split producer kernel)",
             flops_per_launch=2.0 * 256 * 2880 * 201088,
             launch_us=r["stage_us"]["rmsnorm_lm_head"]))

@@ -11,45 +11,48 @@
 // ready B-operand fragments: one 1 KB fragment per (16-lane K block, term,
 // 32-row tile), lane 32 h + n holding row n at K lanes 8 h .. 8 h + 7.
 //
-// One launch covers a chunk of 32 RT batch rows for the whole vocabulary,
-// with one persistent workgroup per CU: RT = 8 (256-row chunks) with tiles
-// of up to MB = 9 blocks above 128 rows, RT = 4 (one 128-row chunk) with
-// tiles of up to 13 blocks from 65 to 128 rows (one 32-row tile per wave
-// leaves the accumulators for the wider tile: 2 passes instead of 3 over
-// the activations).  The vocabulary is cut into 32-column
-// blocks and the blocks into npass * P tiles of equal width (to within one
-// block, at most MB blocks); workgroup w takes tiles w, w + P, w + 2P, ...,
-// so at any time the P workgroups read one contiguous column range of every
-// weight row (whole DRAM pages together: measured 6.9 TB/s for the weight
-// stream alone against 5.3 TB/s with contiguous per-workgroup ranges).
+// One launch covers a chunk of batch rows for the whole vocabulary, with one
+// persistent workgroup per CU of 8 waves, two per SIMD, each wave owning one
+// 32-row tile of the chunk and a column part of every tile, in accumulators
+// of 32 x 32 (at most 13 blocks: 208 of the wave's 256 registers).  Two
+// shapes: CPN = 2 column parts (a 128-row chunk; wave w owns rows
+// 32 (w % 4) .. + 31 and the first (w < 4) or second half of the tile's
+// blocks), used up to 128 rows, and CPN = 1 (a 256-row chunk; wave w owns
+// rows 32 w .. + 31 and all of the tile's blocks), used above.  Either way
+// the tiles hold up to MB = 13 blocks, so GPT-OSS's vocabulary takes 2
+// passes over the activations instead of the 3 that 9-block tiles need (a
+// third fewer activation bytes re-read from L2).  The vocabulary is cut
+// into 32-column blocks and the blocks into npass * P tiles of equal width
+// (to within one block, at most MB blocks); workgroup w takes tiles w,
+// w + P, w + 2P, ..., so at any time the P workgroups read one contiguous
+// column range of every weight row (whole DRAM pages together: measured
+// 6.9 TB/s for the weight stream alone against 5.3 TB/s with contiguous
+// per-workgroup ranges).
 //
-// A workgroup has 8 waves, two per SIMD.  Wave w owns NB = RT / 4 32-row
-// tiles of the chunk (rows 32 NB (w % 4) .. + 32 NB - 1) and the first
-// (w < 4) or second half of the tile's blocks, in accumulators of 32 x 32.
-// A wave whose rows are all padding (a short last chunk) skips its reads
-// and MFMAs and only
-// takes part in the copies and barriers; one with one real 32-row tile
-// multiplies only that one.  Per K-step of 16 hidden lanes the
-// tile's weight [16 x 32 W] goes to an LDS ring of NSW stages, NSW - 1 steps
-// ahead, and the step's activation fragments (RT tiles x NT terms) to a ring
-// of NSA stages, NSA - 1 steps ahead, by direct global-to-LDS copies: waves
-// 0-3 copy the weight, waves 4-7 the activations, so each wave waits only on
-// one stream (vector memory operations complete in issue order per wave: one
-// wave carrying both the slow weight stream and the fast activation stream
-// made the fast one wait for the slow one, 320 us against 227 us for the
-// data movement of one gbs-256 call).  One barrier per step publishes the
-// stage and retires the reads of the stage the next copies overwrite; it is
-// the bare s_barrier, since a workgroup fence before it would drain every
-// copy in flight.  The copies are issued as inline assembly: a compiler that
-// sees them would make every LDS read of the wave wait for every copy in
-// flight.  They write only LDS, so no register of the wave is pending.
+// A wave whose rows are all padding (a short last chunk) skips its reads and
+// MFMAs and only takes part in the copies and barriers.  Per K-step of 16
+// hidden lanes the tile's weight [16 x 32 W] goes to an LDS ring of NSW
+// stages, NSW - 1 steps ahead, and the step's activation fragments (one per
+// 32-row tile and term) to a ring of NSA stages, NSA - 1 steps ahead, by
+// direct global-to-LDS copies: waves 0-3 copy the weight, waves 4-7 the
+// activations, so each wave waits only on one stream (vector memory
+// operations complete in issue order per wave: one wave carrying both the
+// slow weight stream and the fast activation stream made the fast one wait
+// for the slow one, 320 us against 227 us for the data movement of one
+// gbs-256 call).  One barrier per step publishes the stage and retires the
+// reads of the stage the next copies overwrite; it is the bare s_barrier,
+// since a workgroup fence before it would drain every copy in flight.  The
+// copies are issued as inline assembly: a compiler that sees them would make
+// every LDS read of the wave wait for every copy in flight.  They write only
+// LDS, so no register of the wave is pending.
 //
-// The two waves of a SIMD are staggered by half a step: between two barriers
-// waves 0-3 read the step's operands and then run its MFMAs, while waves
-// 4-7 first run the MFMAs of the operands they read before the barrier and
-// then read the step's; so one wave's LDS reads overlap the other's MFMAs
-// and the matrix core of the SIMD stays busy.  (Reading and then multiplying
-// in every wave cost 429 us against a 240 us MFMA floor.)
+// In the two-part shape the two waves of a SIMD are staggered by half a
+// step: between two barriers waves 0-3 read the step's operands and then run
+// its MFMAs, while waves 4-7 first run the MFMAs of the operands they read
+// before the barrier and then read the step's, so one wave's LDS reads
+// overlap the other's MFMAs.  The one-part shape cannot hold a whole step's
+// operands across a barrier next to 208 accumulators, so every wave reads
+// and multiplies block by block, the reads a few blocks ahead.
 //
 // LDS layouts: a weight stage holds 16 rows of 32 MB columns at a row pitch
 // of 64 MB bytes padded to 64 mod 256, so the 8 row segments that 32 lanes of
@@ -65,11 +68,12 @@
 // l holds column 8 i + 4 (l / 32) + e of the block for row l % 32, so each
 // lane stores float4s; the 64-column key groups' maxima go to gkey (a plain
 // store when both 32-column blocks of the group belong to the wave, an atomic
-// maximum into the cleared entry when the group straddles two halves or two
+// maximum into the cleared entry when the group straddles two parts or two
 // tiles).
 //
 // Determinism: every output element is one fixed sequence of MFMAs (K-steps
-// in order, terms in order), the same for every column and row.
+// in order, terms in order), the same for every column and row and in both
+// shapes.
 #include "lds_copy.h"
 
 namespace tail {
@@ -77,11 +81,10 @@ namespace {
 
 using namespace mfma32;
 
-template <int NT, int NBT, int MB, int NSW, int NSA>
+template <int NT, int MB, int NSW, int NSA, int CPN>
 struct RCfg {
-  static constexpr int NB = NBT;                         // 32-row tiles per wave (1 or 2)
-  static constexpr int RT = 4 * NB;                      // row tiles per chunk (128 or 256 rows)
-  static constexpr int CHUNK = 32 * RT;
+  static constexpr int RT = 8 / CPN;                     // 32-row tiles per chunk (one per row group)
+  static constexpr int CHUNK = 32 * RT;                  // 128 or 256 rows
   static constexpr int WPITCH = weight_pitch(MB);
   static constexpr int WCH = WPITCH / 16;                // 16-byte chunks per weight row
   static constexpr int WSTAGE = 16 * WPITCH;
@@ -91,10 +94,10 @@ struct RCfg {
   static constexpr int APER = AFR / 4;                   // activation copies per wave
   static constexpr int ASTAGE = AFR * 1024;
   static constexpr int LDS = NSW * WSTAGE + NSA * ASTAGE;
-  static constexpr int HB = (MB + 1) / 2;                // most blocks of a half
-  static_assert(WSTAGE % 1024 == 0 && WPITCH % 256 == 64 && AFR % 4 == 0 && NSW >= 2 &&
-                    NSA >= 2 && WPER * (NSW - 2) < 64 && APER * (NSA - 2) < 64 &&
-                    LDS <= 160 * 1024,
+  static constexpr int HB = (MB + CPN - 1) / CPN;        // most blocks of a column part
+  static_assert((CPN == 1 || CPN == 2) && WSTAGE % 1024 == 0 && WPITCH % 256 == 64 &&
+                    WCH <= 64 && AFR % 4 == 0 && NSW >= 2 && NSA >= 2 &&
+                    WPER * (NSW - 2) < 64 && APER * (NSA - 2) < 64 && LDS <= 160 * 1024,
                 "tile");
 };
 
@@ -174,36 +177,37 @@ struct Copier {
 };
 
 // One wave's part of one tile (steps q0 .. q0 + nks - 1): WC blocks starting
-// at block cb0 of the tile, rows 64 rg .. 64 rg + 63.  LAG: the wave runs each
+// at block cb0 of the tile, row tile rg of the chunk.  LAG: the wave runs each
 // step's MFMAs after the next barrier (see above).
-template <typename C, typename CP, int NT, int NSW, int NSA, int WC, int NV, bool LAG>
+template <typename C, typename CP, int NT, int NSW, int NSA, int WC, bool LAG>
 __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, const lds_u8* aring,
-                                          int rg, int lane, int q0, int blk0, int cb0, int tstart,
-                                          int twidth, const float (&scale)[C::NB], int b0, int gbs,
-                                          int V, float* __restrict__ logits,
+                                          int rg, int lane, int q0, int blk0, int cb0,
+                                          float scale, int b0, int gbs, int V,
+                                          float* __restrict__ logits,
                                           uint32_t* __restrict__ gkey, int groups) {
-  constexpr int NB = C::NB;
   const int tr_off = tr_lane_offset<C::WPITCH>(lane) + cb0 * 64;
-  const int b_off = (rg * NB * 64 + lane) * 16;
+  const int b_off = (rg * 64 + lane) * 16;
   const int nks = cp.G.nks;
 
-  f32x16 acc[NV][WC];
+  f32x16 acc[WC];
 #pragma unroll
-  for (int nb = 0; nb < NV; ++nb)
+  for (int c = 0; c < WC; ++c)
 #pragma unroll
-    for (int c = 0; c < WC; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[nb][c][e] = 0.0f;
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.0f;
 
-  bf16x8 bop[NV][NT], aop[WC];
+  bf16x8 bop[NT], aop[WC];
   auto read = [&](int q) {
-    const lds_u8* wst = wring + (q % NSW) * C::WSTAGE + tr_off;
-    const lds_u8* ast = aring + (q % NSA) * C::ASTAGE + b_off;
+    int tro = tr_off, bo = b_off;
+    // with 208 accumulators, the compiler would otherwise keep every
+    // block's LDS address in a register of its own (hoisted out of the K
+    // loop) and spill; opaque per-step offsets make it fold the block
+    // offsets into the reads' immediate fields
+    if constexpr (WC > 7) asm volatile("" : "+v"(tro), "+v"(bo));
+    const lds_u8* wst = wring + (q % NSW) * C::WSTAGE + tro;
+    const lds_u8* ast = aring + (q % NSA) * C::ASTAGE + bo;
 #pragma unroll
-    for (int nb = 0; nb < NV; ++nb)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        bop[nb][t] = *reinterpret_cast<const lds_bf16x8*>(ast + (t * C::RT + nb) * 1024);
+    for (int t = 0; t < NT; ++t)
+      bop[t] = *reinterpret_cast<const lds_bf16x8*>(ast + t * C::RT * 1024);
 #pragma unroll
     for (int c = 0; c < WC; ++c) aop[c] = weight_operand<C::WPITCH>(wst + c * 64);
   };
@@ -212,9 +216,7 @@ __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, con
     for (int c = 0; c < WC; ++c)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int nb = 0; nb < NV; ++nb)
-          acc[nb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[c], bop[nb][t], acc[nb][c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[c], bop[t], acc[c], 0, 0, 0);
   };
 
   for (int ks = 0; ks < nks; ++ks) {
@@ -232,21 +234,16 @@ __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, con
   if constexpr (LAG) mma();
 
   // epilogue: scaled logits, key-group maxima
-#pragma unroll
-  for (int nb = 0; nb < NV; ++nb) {
-    const int b = b0 + (rg * NB + nb) * 32 + (lane & 31);
-    store_tile<WC>(acc[nb], scale[nb], b, b < gbs, blk0, cp.G.nblk, lane, V, logits, gkey, groups);
-  }
-  (void)tstart;
-  (void)twidth;
+  const int b = b0 + rg * 32 + (lane & 31);
+  store_tile<WC>(acc, scale, b, b < gbs, blk0, cp.G.nblk, lane, V, logits, gkey, groups);
 }
 
-template <int NT, int NB, int MB, int NSW, int NSA>
+template <int NT, int MB, int NSW, int NSA, int CPN>
 __global__ __launch_bounds__(512, 1) void rows_kernel(
     const uint16_t* __restrict__ act, int nrt, int Kp, const uint16_t* __restrict__ w, int V, int K,
     int pad_s, FastDiv pdiv, const float* __restrict__ row_scale, int gbs, int b0,
     float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups, int npass) {
-  using C = RCfg<NT, NB, MB, NSW, NSA>;
+  using C = RCfg<NT, MB, NSW, NSA, CPN>;
   using CP = Copier<C, NT, NSW, NSA>;
   __shared__ __align__(1024) unsigned char smem[C::LDS];
   const int lane = threadIdx.x & 63;
@@ -259,53 +256,40 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
   const CP cp{G, wring_addr, wring_addr + uint32_t(NSW * C::WSTAGE), wave, lane, act, nrt, w, V,
               K, pad_s, pdiv, b0};
 
-  const int rg = wave & 3, half = wave >> 2;
-  // this wave's 32-row tiles that hold rows of the batch (the others are
-  // padding: their reads and MFMAs are skipped)
-  const int nv = min(max((gbs - b0 + 31) / 32 - NB * rg, 0), NB);
-  float scale[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int b = b0 + (rg * NB + nb) * 32 + (lane & 31);
-    scale[nb] = (b < gbs && row_scale) ? row_scale[b] : 1.0f;
-  }
-  // the scales have arrived before the first copy is issued
+  // row tile and column part of this wave
+  const int rg = CPN == 2 ? (wave & 3) : wave, part = CPN == 2 ? (wave >> 2) : 0;
+  // a 32-row tile that holds no row of the batch is padding: its reads and
+  // MFMAs are skipped
+  const bool real = b0 + rg * 32 < gbs;
+  const int b = b0 + rg * 32 + (lane & 31);
+  const float scale = (b < gbs && row_scale) ? row_scale[b] : 1.0f;
+  // the scale has arrived before the first copy is issued
   wait_vm<0>();
   for (int p = 0; p < cp.ahead() && p < G.total; ++p) cp.issue(p);
 
   for (int j = 0; j < G.ntl; ++j) {
     int start, width;
     G.tile(j, start, width);
-    const int w0 = (width + 1) / 2;
-    const int cb0 = half ? w0 : 0, wc = half ? width - w0 : w0;
+    const int w0 = CPN == 2 ? (width + 1) / 2 : width;
+    const int cb0 = part ? w0 : 0, wc = part ? width - w0 : w0;
     const int q0 = j * G.nks;
-#define TAIL_ROWS_PART_NV(WW, NVV)                                                             \
-  if (half)                                                                                     \
-    tile_part<C, CP, NT, NSW, NSA, WW, NVV, true>(cp, wring, aring, rg, lane, q0, start + cb0,  \
-                                                  cb0, start, width, scale, b0, gbs, V, logits, \
-                                                  gkey, groups);                                \
-  else                                                                                          \
-    tile_part<C, CP, NT, NSW, NSA, WW, NVV, false>(cp, wring, aring, rg, lane, q0, start + cb0, \
-                                                   cb0, start, width, scale, b0, gbs, V, logits,\
-                                                   gkey, groups);
-#define TAIL_ROWS_PART(WW)                                                                       \
-  case WW:                                                                                       \
-    if constexpr (WW <= C::HB) {                                                                 \
-      if constexpr (NB == 2) {                                                                   \
-        if (nv == 2) {                                                                           \
-          TAIL_ROWS_PART_NV(WW, 2)                                                               \
-        } else {                                                                                 \
-          TAIL_ROWS_PART_NV(WW, 1)                                                               \
-        }                                                                                        \
-      } else {                                                                                   \
-        TAIL_ROWS_PART_NV(WW, 1)                                                                 \
-      }                                                                                          \
-    }                                                                                            \
+#define TAIL_ROWS_PART(WW)                                                                     \
+  case WW:                                                                                     \
+    if constexpr (WW <= C::HB) {                                                               \
+      if (CPN == 2 && part)                                                                    \
+        tile_part<C, CP, NT, NSW, NSA, WW, CPN == 2>(cp, wring, aring, rg, lane, q0,           \
+                                                     start + cb0, cb0, scale, b0, gbs, V,      \
+                                                     logits, gkey, groups);                    \
+      else                                                                                     \
+        tile_part<C, CP, NT, NSW, NSA, WW, false>(cp, wring, aring, rg, lane, q0, start + cb0, \
+                                                  cb0, scale, b0, gbs, V, logits, gkey,        \
+                                                  groups);                                     \
+    }                                                                                          \
     break;
-    // a one-block tile leaves the second half empty, and a short last chunk
-    // leaves the waves of its all-padding 32-row tiles idle:
-    // barriers (and their share of the copies) only
-    switch (nv == 0 ? 0 : wc) {
+    // a one-block tile leaves the second part empty, and a short last chunk
+    // leaves the waves of its all-padding 32-row tiles idle: barriers (and
+    // their share of the copies) only
+    switch (real ? wc : 0) {
       case 0:
         for (int ks = 0; ks < G.nks; ++ks) {
           cp.step(q0 + ks);
@@ -313,19 +297,19 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
         }
         break;
       TAIL_ROWS_PART(1) TAIL_ROWS_PART(2) TAIL_ROWS_PART(3) TAIL_ROWS_PART(4) TAIL_ROWS_PART(5)
-      TAIL_ROWS_PART(6) TAIL_ROWS_PART(7)
+      TAIL_ROWS_PART(6) TAIL_ROWS_PART(7) TAIL_ROWS_PART(8) TAIL_ROWS_PART(9) TAIL_ROWS_PART(10)
+      TAIL_ROWS_PART(11) TAIL_ROWS_PART(12) TAIL_ROWS_PART(13)
       default: break;
     }
-#undef TAIL_ROWS_PART_NV
 #undef TAIL_ROWS_PART
   }
 }
 
-template <int NT, int NB, int MB, int NSW, int NSA>
+template <int NT, int MB, int NSW, int NSA, int CPN>
 hipError_t launch_rows_cfg(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V,
                            int K, int pad_s, const float* row_scale, int gbs, float* logits,
                            uint32_t* gkey, hipStream_t st) {
-  auto kern = rows_kernel<NT, NB, MB, NSW, NSA>;
+  auto kern = rows_kernel<NT, MB, NSW, NSA, CPN>;
   static std::once_flag once[kMaxDevices];
   static int cus_cache[kMaxDevices];
   const int cus = per_device(once, cus_cache, [&](int dev) {
@@ -339,7 +323,7 @@ hipError_t launch_rows_cfg(const uint16_t* act, int rows_pad, int Kp, const uint
   const int P = nblk < cus ? nblk : cus;
   const int npass = (nblk + P * MB - 1) / (P * MB);
   const int groups = (V + kFusedGroup - 1) / kFusedGroup;
-  for (int b0 = 0; b0 < gbs; b0 += RCfg<NT, NB, MB, NSW, NSA>::CHUNK) {
+  for (int b0 = 0; b0 < gbs; b0 += RCfg<NT, MB, NSW, NSA, CPN>::CHUNK) {
     hipLaunchKernelGGL(kern, dim3(P), dim3(512), 0, st, act, rows_pad / 32, Kp, w, V, K, pad_s,
                        pdiv, row_scale, gbs, b0, logits, gkey, groups, npass);
     const hipError_t e = hipGetLastError();
@@ -353,24 +337,24 @@ hipError_t launch_rows_cfg(const uint16_t* act, int rows_pad, int Kp, const uint
 hipError_t launch_lm_head_rows(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,
                                int V, int K, int pad_s, const float* row_scale, int gbs,
                                float* logits, uint32_t* gkey, hipStream_t st) {
-  // up to 128 rows: 128-row chunks of one 32-row tile per wave, whose
-  // accumulators leave room for 13-block tiles (2 passes for GPT-OSS);
-  // above: 256-row chunks of two tiles per wave and 9-block tiles (3 passes)
+  // up to 128 rows: one 128-row chunk in two column parts; above: 256-row
+  // chunks in one part.  Tiles of up to 13 blocks either way (2 passes for
+  // GPT-OSS); ring depths from sweeps.
   if (gbs <= 128) {
     if (nt == 2)
-      return launch_rows_cfg<2, 1, 13, 8, 4>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs,
+      return launch_rows_cfg<2, 13, 8, 4, 2>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs,
                                              logits, gkey, st);
     if (nt == 1)
-      return launch_rows_cfg<1, 1, 13, 8, 6>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs,
+      return launch_rows_cfg<1, 13, 8, 6, 2>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs,
                                              logits, gkey, st);
     return hipErrorInvalidValue;
   }
   if (nt == 2)
-    return launch_rows_cfg<2, 2, 9, 8, 4>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs, logits,
-                                          gkey, st);
+    return launch_rows_cfg<2, 13, 8, 3, 1>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs,
+                                           logits, gkey, st);
   if (nt == 1)
-    return launch_rows_cfg<1, 2, 9, 8, 6>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs, logits,
-                                          gkey, st);
+    return launch_rows_cfg<1, 13, 8, 5, 1>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs,
+                                           logits, gkey, st);
   return hipErrorInvalidValue;
 }
 

@@ -184,16 +184,17 @@ def test_rows_across_path_boundaries(page):
                                      (129, 64, 16448), (250, 64, 16448), (200, 96, 65600)])
 def test_lm_head_persistent_uneven_groups(page, gbs, H, V):
     """Above 128 rows (the 32x32x16 large-batch kernel: one workgroup per CU,
-    the vocabulary's 32-column blocks cut into tiles of at most 9 blocks that
-    the workgroups take in interleaved passes), on vocabularies whose blocks
-    do not divide evenly over the tiles, the logits meet the parity bar and
-    columns duplicated far apart give bitwise-equal logits (every element
-    takes its full K in order).  196928 columns: 6154 blocks in 3 passes of
-    256 tiles, 10 of 9 blocks and 758 of 8; 16448: 514 blocks, one pass, 2
-    tiles of 3 and 254 of 2 (the second half of a 2-block tile is one
-    block); 65600: 2050 blocks, 2 tiles of 9 and 254 of 8.  193 rows leave
-    the last 32-row tile one row; 150 and 129 leave rows padding; K = 200
-    pads to 256 with clamped weight rows; K = 64 gives four K-steps."""
+    256-row chunks, the vocabulary's 32-column blocks cut into tiles of at
+    most 13 blocks that the workgroups take in interleaved passes), on
+    vocabularies whose blocks do not divide evenly over the tiles, the logits
+    meet the parity bar and columns duplicated far apart give bitwise-equal
+    logits (every element takes its full K in order).  196928 columns: 6154
+    blocks in 2 passes of 256 tiles, 10 of 13 blocks and 502 of 12; 16448:
+    514 blocks, one pass, 2 tiles of 3 and 254 of 2; 65600: 2050 blocks, 2
+    tiles of 9 and 254 of 8.  224, 193, 150 and 129 rows leave whole 32-row
+    tiles of padding (their waves only copy); 193 leaves the last real tile
+    one row and 250 six rows short; K = 200 pads to 256 with clamped weight
+    rows; K = 64 gives four K-steps."""
     rng = np.random.default_rng(11 + page + gbs)
     w = bf16_bits(rng.standard_normal((H, V)) * 0.05)
     groups = V // 64
