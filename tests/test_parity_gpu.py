@@ -71,7 +71,10 @@ def test_rmsnorm(dtype, shape, deferred):
                                             (17, 96, 96, 776, False), (33, 320, 320, 1288, False),
                                             (64, 3072, 2880, 2056, True), (65, 100, 100, 512, False),
                                             (130, 2880, 2880, 800, False), (256, 700, 700, 1544, False),
-                                            (300, 64, 64, 264, False)])
+                                            (300, 64, 64, 264, False),
+                                            # pad lanes on the large-batch kernel's 128-row and
+                                            # 256-row chunk shapes (weight rows copied by index)
+                                            (96, 3072, 2880, 1544, True), (200, 3072, 2880, 2056, True)])
 def test_lm_head(gbs, H, H_u, V, zp):
     rng = np.random.default_rng(V + gbs)
     pad = oracle.pad_mask(H, H_u, zp)
@@ -92,7 +95,8 @@ def test_lm_head(gbs, H, H_u, V, zp):
     (1, 2880, 2880, 4096, False, synth.DT_BF16, True), (1, 2880, 2880, 4096, False, synth.DT_BF16, False),
     (3, 3072, 2880, 2056, True, synth.DT_F16, True), (4, 300, 300, 1160, False, synth.DT_F32, False),
     (8, 640, 640, 2048, False, synth.DT_F32, True), (40, 3072, 2880, 1032, True, synth.DT_F16, False),
-    (130, 256, 256, 520, False, synth.DT_BF16, True)])
+    (130, 256, 256, 520, False, synth.DT_BF16, True),
+    (257, 3072, 2880, 1032, True, synth.DT_F16, True)])   # two chunks, the second of one row
 def test_rmsnorm_lm_head(gbs, H, H_u, V, zp, dtype, deferred):
     rng = np.random.default_rng(V * 3 + gbs)
     pad = oracle.pad_mask(H, H_u, zp)
@@ -363,12 +367,13 @@ def test_workload_parity_other_seeds(cid, seed):
     (5, 300, 300, 8000, 64, False, synth.DT_BF16),   # ragged last slab
     (9, 640, 640, 2048, 1024, False, synth.DT_F32),  # k = TAIL_K_MAX, two lm_head passes
     (1, 128, 128, 64, 64, False, synth.DT_F32),      # k = V
-    # above 192 rows: the persistent lm_head, whose leftover items end in a
-    # partial group (V not a multiple of 64) and write its maximum; 140 rows:
-    # a 128-row chunk and a 12-row chunk on the per-tile kernel
+    # above 128 rows: the large-batch kernel's 256-row chunks, the last
+    # 64-column group partial (V not a multiple of 64); 140 and 160 rows leave
+    # whole 32-row tiles of padding
     (200, 64, 64, 16456, 256, False, synth.DT_F32),
     (240, 96, 96, 65608, 64, False, synth.DT_BF16),
     (140, 64, 64, 16456, 256, False, synth.DT_F32),
+    (160, 96, 90, 12296, 256, True, synth.DT_BF16),   # pad lanes on the 256-row chunk shape
 ])
 def test_forward_small_shapes(gbs, H, H_u, V, k, zp, dtype):
     rng = np.random.default_rng(V * 31 + k)
