@@ -18,10 +18,11 @@
 // shapes: CPN = 2 column parts (a 128-row chunk; wave w owns rows
 // 32 (w % 4) .. + 31 and the first (w < 4) or second half of the tile's
 // blocks), used up to 128 rows, and CPN = 1 (a 256-row chunk; wave w owns
-// rows 32 w .. + 31 and all of the tile's blocks), used above.  Either way
-// the tiles hold up to MB = 13 blocks, so GPT-OSS's vocabulary takes 2
-// passes over the activations instead of the 3 that 9-block tiles need (a
-// third fewer activation bytes re-read from L2).  The vocabulary is cut
+// rows 32 w .. + 31 and all of the tile's blocks, except that a two-term
+// chunk of 5 or 6 real tiles halves some of them, see below), used above.
+// Either way the tiles hold up to MB = 13 blocks, so GPT-OSS's vocabulary
+// takes 2 passes over the activations instead of the 3 that 9-block tiles
+// need (a third fewer activation bytes re-read from L2).  The vocabulary is cut
 // into 32-column blocks and the blocks into npass * P tiles of equal width
 // (to within one block, at most MB blocks); workgroup w takes tiles w,
 // w + P, w + 2P, ..., so at any time the P workgroups read one contiguous
@@ -256,8 +257,30 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
   const CP cp{G, wring_addr, wring_addr + uint32_t(NSW * C::WSTAGE), wave, lane, act, nrt, w, V,
               K, pad_s, pdiv, b0};
 
-  // row tile and column part of this wave
-  const int rg = CPN == 2 ? (wave & 3) : wave, part = CPN == 2 ? (wave >> 2) : 0;
+  // row tile and column part of this wave (part 0: the tile's first half, 1:
+  // its second half, 2: the whole tile)
+  int rg = CPN == 2 ? (wave & 3) : wave, part = CPN == 2 ? (wave >> 2) : 2;
+  if constexpr (CPN == 1 && NT == 2) {
+    // 5 or 6 real tiles in a 256-row chunk: whole-tile waves would leave two
+    // SIMDs running two whole tiles each while others idle.  So 8 - nreal
+    // tiles are halved instead: waves 0 .. 2 nreal - 9 take the whole tiles
+    // 8 - nreal .., and each of the others a half, the SIMD partners (w,
+    // w + 4) of the whole-tile waves first, so no SIMD runs more than one
+    // whole tile and one half.  (Not in the one-term kernel, whose
+    // registers it would overrun by a few.)
+    const int nreal = min(C::RT, nrt - b0 / 32);
+    if (nreal == 5 || nreal == 6) {
+      const int nwhole = 2 * nreal - 8;  // 2 or 4
+      if (wave < nwhole) {
+        rg = 8 - nreal + wave;
+      } else {
+        // half-tile waves in the order 4, 5, 6, 7, then nwhole .. 3
+        const int order = wave >= 4 ? wave - 4 : wave - nwhole + 4;
+        rg = order >> 1;
+        part = order & 1;
+      }
+    }
+  }
   // a 32-row tile that holds no row of the batch is padding: its reads and
   // MFMAs are skipped
   const bool real = b0 + rg * 32 < gbs;
@@ -270,8 +293,8 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
   for (int j = 0; j < G.ntl; ++j) {
     int start, width;
     G.tile(j, start, width);
-    const int w0 = CPN == 2 ? (width + 1) / 2 : width;
-    const int cb0 = part ? w0 : 0, wc = part ? width - w0 : w0;
+    const int w0 = part == 2 ? width : (width + 1) / 2;
+    const int cb0 = part == 1 ? w0 : 0, wc = part == 1 ? width - w0 : w0;
     const int q0 = j * G.nks;
 #define TAIL_ROWS_PART(WW)                                                                     \
   case WW:                                                                                     \
