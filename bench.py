@@ -93,7 +93,8 @@ def copy_calibration():
 # the sources the gbs-1 RMSNorm + lm_head kernel and the large-batch
 # matrix-core kernel (with its activation producer) are built from
 GEMV_SOURCES = ("lm_head_gemv.hip", "tail_internal.h")
-ROWS_SOURCES = ("lm_head_rows.hip", "lds_copy.h", "rmsnorm.hip", "tail_internal.h")
+ROWS_SOURCES = ("lm_head_rows.hip", "lds_copy.h", "rmsnorm.hip", "tail_internal.h", "select_row.h",
+                "sampler_row.h")
 
 
 def kernel_source_hash(sources=GEMV_SOURCES):

@@ -75,7 +75,23 @@
 // Determinism: every output element is one fixed sequence of MFMAs (K-steps
 // in order, terms in order), the same for every column and row and in both
 // shapes.
+//
+// Fused top-k and sampler (optional, FusedSelect): the page's tail is one
+// kernel from the RMSNorm to the sampled token (GPT-OSS tail API page,
+// Background).  Here the workgroups of a launch, one per CU and normally all
+// resident at once, finish their tiles, then meet at a grid barrier (their
+// logit and group-maximum stores written back device-wide, one lane per
+// workgroup counts the workgroup in on an arrival counter and polls it until
+// all have arrived, as in the leader-follower barrier of the Triton
+// megakernel page), and then take the launch's rows one at a time from a
+// second counter and run the select of select_row.h on each with all 512
+// threads, the rings' LDS reused for its lists.  The poll is bounded: a
+// workgroup that stops polling leaves the rows to the others, and the last
+// one to arrive never polls, so every row is selected whether or not the
+// workgroups were resident together, and every workgroup ends.  The results
+// are bitwise those of the separate select launch.
 #include "lds_copy.h"
+#include "select_row.h"
 
 namespace tail {
 namespace {
@@ -239,18 +255,78 @@ __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, con
   store_tile<WC>(acc, scale, b, b < gbs, blk0, cp.G.nblk, lane, V, logits, gkey, groups);
 }
 
+// The grid barrier and the select phase (see above) over rows b0 .. b0 +
+// nrows - 1; smem holds at least a SelShared and one more word.  MIRROR: the
+// page-precision mode's bf16 ranking.  tid = 64 wave + lane (the tile phase
+// keeps both live, so no register of its own carries the work-item id).
+template <bool MIRROR>
+__device__ __forceinline__ void fused_select(unsigned char* smem, int tid, const FusedSelect& fs,
+                                             uint32_t* sync, const float* logits,
+                                             const uint32_t* gkey, int V, int b0, int nrows) {
+  SelShared& s = *reinterpret_cast<SelShared*>(smem);
+  int* const word = reinterpret_cast<int*>(smem + sizeof(SelShared));
+  // arrival: every wave waits until its stores have reached the L2, then one
+  // lane writes the L2 back device-wide (one release per workgroup: a release
+  // in every wave, each writing the whole L2 back, cost about 35 us at 256
+  // rows) and counts the workgroup in.  Leaving, that lane invalidates the
+  // caches its CU and L2 hold for the other workgroups' results (once for
+  // all waves of the CU).
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    uint32_t n = __hip_atomic_fetch_add(&sync[0], 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    for (int i = 0; n < gridDim.x && i < fs.spin; ++i) {
+      __builtin_amdgcn_s_sleep(8);
+      n = __hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *word = n >= gridDim.x;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(*word)) return;  // the rows are left to the others
+  // the sampler's candidates per lane, as the standalone select launches it
+  const int pc = fs.k <= 64 ? 1 : fs.k <= 128 ? 2 : fs.k <= 256 ? 4 : fs.k <= 512 ? 8 : 16;
+  auto sample = [&](SelShared& sh, const RowParams& prm, int lane) -> int32_t {
+#define TAIL_FUSED_SAMPLE(PC) \
+  return sample_row_wave<PC>(sh.top_v, sh.top_i, fs.k, prm.top_k, prm.top_p, prm.temp, prm.u, lane)
+    switch (pc) {
+      case 1: TAIL_FUSED_SAMPLE(1);
+      case 2: TAIL_FUSED_SAMPLE(2);
+      case 4: TAIL_FUSED_SAMPLE(4);
+      case 8: TAIL_FUSED_SAMPLE(8);
+      default: TAIL_FUSED_SAMPLE(16);
+    }
+#undef TAIL_FUSED_SAMPLE
+  };
+  for (;;) {
+    __syncthreads();  // the previous row's lists have been read
+    if (tid == 0)
+      *word = int(__hip_atomic_fetch_add(&sync[1], 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+    const int r = __builtin_amdgcn_readfirstlane(*word);
+    if (r >= nrows) break;
+    select_row<512, MIRROR>(s, tid, b0 + r, logits, V, fs.gs, fs.groups, fs.k, gkey, 0, fs.vals, fs.idx,
+                            nullptr, fs.params, fs.ncols, fs.tokens, sample);
+  }
+}
+
 template <int NT, int MB, int NSW, int NSA, int CPN>
 __global__ __launch_bounds__(512, 1) void rows_kernel(
     const uint16_t* __restrict__ act, int nrt, int Kp, const uint16_t* __restrict__ w, int V, int K,
     int pad_s, FastDiv pdiv, const float* __restrict__ row_scale, int gbs, int b0,
-    float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups, int npass) {
+    float* __restrict__ logits, uint32_t* __restrict__ gkey, int groups, int npass,
+    const FusedSelect* __restrict__ fsp) {
   using C = RCfg<NT, MB, NSW, NSA, CPN>;
   using CP = Copier<C, NT, NSW, NSA>;
+  static_assert(sizeof(SelShared) + 4 <= C::LDS, "select lists in the rings' LDS");
   __shared__ __align__(1024) unsigned char smem[C::LDS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const TileGeom G(V, Kp, npass);
-  if (G.total == 0) return;  // the whole workgroup
+  if (G.total == 0 && fsp == nullptr) return;  // the whole workgroup
   lds_u8* const wring = (lds_u8*)smem;
   lds_u8* const aring = wring + NSW * C::WSTAGE;
   const uint32_t wring_addr = uint32_t(reinterpret_cast<uintptr_t>(wring));
@@ -326,12 +402,22 @@ __global__ __launch_bounds__(512, 1) void rows_kernel(
     }
 #undef TAIL_ROWS_PART
   }
+  // not in the one-term one-part kernel, which uses all 256 registers and
+  // spills with any code after its tiles (rows_fuse_select)
+  if constexpr (NT == 2 || CPN == 2) {
+    if (fsp != nullptr) {
+      const FusedSelect fs = *fsp;
+      // each launch of a multi-launch batch has its own two counters
+      fused_select<NT == 1>(smem, wave * 64 + int(__lane_id()), fs, fs.sync + 2 * (b0 / C::CHUNK),
+                            logits, gkey, V, b0, min(gbs - b0, C::CHUNK));
+    }
+  }
 }
 
 template <int NT, int MB, int NSW, int NSA, int CPN>
 hipError_t launch_rows_cfg(const uint16_t* act, int rows_pad, int Kp, const uint16_t* w, int V,
                            int K, int pad_s, const float* row_scale, int gbs, float* logits,
-                           uint32_t* gkey, hipStream_t st) {
+                           uint32_t* gkey, const FusedSelect* fs, hipStream_t st) {
   auto kern = rows_kernel<NT, MB, NSW, NSA, CPN>;
   static std::once_flag once[kMaxDevices];
   static int cus_cache[kMaxDevices];
@@ -348,7 +434,7 @@ hipError_t launch_rows_cfg(const uint16_t* act, int rows_pad, int Kp, const uint
   const int groups = (V + kFusedGroup - 1) / kFusedGroup;
   for (int b0 = 0; b0 < gbs; b0 += RCfg<NT, MB, NSW, NSA, CPN>::CHUNK) {
     hipLaunchKernelGGL(kern, dim3(P), dim3(512), 0, st, act, rows_pad / 32, Kp, w, V, K, pad_s,
-                       pdiv, row_scale, gbs, b0, logits, gkey, groups, npass);
+                       pdiv, row_scale, gbs, b0, logits, gkey, groups, npass, fs);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -359,25 +445,26 @@ hipError_t launch_rows_cfg(const uint16_t* act, int rows_pad, int Kp, const uint
 
 hipError_t launch_lm_head_rows(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,
                                int V, int K, int pad_s, const float* row_scale, int gbs,
-                               float* logits, uint32_t* gkey, hipStream_t st) {
+                               float* logits, uint32_t* gkey, const FusedSelect* fs,
+                               hipStream_t st) {
   // up to 128 rows: one 128-row chunk in two column parts; above: 256-row
   // chunks in one part.  Tiles of up to 13 blocks either way (2 passes for
   // GPT-OSS); ring depths from sweeps.
   if (gbs <= 128) {
     if (nt == 2)
       return launch_rows_cfg<2, 13, 8, 4, 2>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs,
-                                             logits, gkey, st);
+                                             logits, gkey, fs, st);
     if (nt == 1)
       return launch_rows_cfg<1, 13, 8, 6, 2>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs,
-                                             logits, gkey, st);
+                                             logits, gkey, fs, st);
     return hipErrorInvalidValue;
   }
   if (nt == 2)
     return launch_rows_cfg<2, 13, 8, 3, 1>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs,
-                                           logits, gkey, st);
+                                           logits, gkey, fs, st);
   if (nt == 1)
     return launch_rows_cfg<1, 13, 8, 5, 1>(act, rows_pad, Kp, w, V, K, pad_s, row_scale, gbs,
-                                           logits, gkey, st);
+                                           logits, gkey, fs, st);
   return hipErrorInvalidValue;
 }
 

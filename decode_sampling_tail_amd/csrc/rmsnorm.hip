@@ -118,7 +118,9 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const void* __restric
 // Each thread produces one 16-byte lane (an "octet") per term.  gz (may be
 // NULL): this row's [groups] entries are cleared (the matrix-core kernels
 // combine the maxima of the key groups that straddle two of their tiles
-// there with atomic maxima).
+// there with atomic maxima); fs_out (may be NULL): row 0 stores the
+// large-batch kernel's select arguments there and clears their counters (its
+// grid barrier's and row queue's).
 __device__ inline uint16_t bf16_rne(float f) { return uint16_t(bf16_rne_bits(__float_as_uint(f))); }
 __device__ inline float bf16_val(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
@@ -136,7 +138,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
                                                          int rows_pad, int Kp,
                                                          uint16_t* __restrict__ act,
                                                          float* __restrict__ r_out,
-                                                         uint32_t* __restrict__ gz, int groups) {
+                                                         uint32_t* __restrict__ gz, int groups,
+                                                         FusedSelect fs, FusedSelect* fs_out) {
   __shared__ double s_part[kThreads / 64];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -152,6 +155,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const void* __restrict_
   };
   if (gz && row < gbs)
     for (int i = tid; i < groups; i += kThreads) gz[size_t(row) * groups + i] = 0u;
+  if (fs_out && row == 0) {
+    if (tid == 0) *fs_out = fs;
+    for (int i = tid; i < fs.nsync; i += kThreads) fs.sync[i] = 0u;
+  }
   if (row >= gbs) {
     for (int o = tid; o < Kp / 8; o += kThreads)
 #pragma unroll
@@ -294,12 +301,12 @@ namespace tail {
 hipError_t launch_split(const void* src, int dtype, bool norm, const float* gamma, int gbs, int H,
                         int H_u, int K, int pad_s, float eps, bool deferred, int nt, int layout,
                         int rows_pad, int Kp, uint16_t* act, float* r, uint32_t* gz, int groups,
-                        hipStream_t st) {
+                        const FusedSelect& fs, FusedSelect* fs_out, hipStream_t st) {
   const FastDiv pdiv = make_fastdiv(pad_s > 1 ? uint32_t(pad_s - 1) : 1u);
   dim3 grid(rows_pad), block(kThreads);
 #define TAIL_SPLIT(DT, NT, NORM, L)                                                              \
   hipLaunchKernelGGL((split_kernel<DT, NT, NORM, L>), grid, block, 0, st, src, gamma, H, H_u, K, \
-                     pad_s, pdiv, eps, int(deferred), gbs, rows_pad, Kp, act, r, gz, groups)
+                     pad_s, pdiv, eps, int(deferred), gbs, rows_pad, Kp, act, r, gz, groups, fs, fs_out)
 #define TAIL_SPLIT_DT(NT, L)                    \
   do {                                          \
     if (!norm) TAIL_SPLIT(0, NT, false, L);     \

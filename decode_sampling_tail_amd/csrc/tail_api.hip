@@ -5,6 +5,7 @@
 #include "tail_internal.h"
 
 #include <math.h>
+#include <stdlib.h>
 
 #define TAIL_API extern "C" __attribute__((visibility("default")))
 
@@ -71,7 +72,7 @@ SplitGeom split_geom(int gbs, int H, int H_u, int pad_s, int V, unsigned flags) 
 }
 
 struct FwdLayout {
-  size_t y, r, act, part, logits, gkey, total;
+  size_t y, r, act, part, logits, gkey, sync, total;
 };
 
 // split-K partials of the lm_head path this batch takes (narrow vocabularies)
@@ -100,6 +101,8 @@ FwdLayout forward_layout(int gbs, int H, int H_u, int pad_s, int V, int k, unsig
   if (!(flags & TAIL_EMIT_LOGITS)) off = align256(off + size_t(gbs) * V * 4);
   L.gkey = off;
   off = align256(off + size_t(gbs) * g.groups * 4);
+  L.sync = off;  // the fused select's arguments, then its counters
+  off = align256(off + sizeof(tail::FusedSelect) + size_t(tail::fused_sync_words(gbs)) * 4);
   L.total = off;
   return L;
 }
@@ -118,11 +121,13 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 
 // RMSNorm + lm_head: fused weight-streaming kernel, or RMSNorm then the
 // weight-streaming kernel, or the bf16-split producer then the matrix cores.
-// y (gbs*H floats) and act (split_geom bytes) are workspace.
+// y (gbs*H floats) and act (split_geom bytes) are workspace.  fs (may be
+// NULL, large-batch kernel only): that kernel also runs the top-k and sampler,
+// with the arguments fs stored by the producer at fs_dev (workspace).
 hipError_t norm_lm_head(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t,
                         int gbs, int H, int H_u, int V, float eps, int ps, unsigned flags, float* y,
                         float* r, uint16_t* act, void* part, float* logits, uint32_t* gkey,
-                        hipStream_t st) {
+                        const tail::FusedSelect* fs, tail::FusedSelect* fs_dev, hipStream_t st) {
   const bool deferred = flags & TAIL_DEFERRED_RMS, page = flags & TAIL_PAGE_PRECISION;
   const SplitGeom sg = split_geom(gbs, H, H_u, ps, V, flags);
   if (tail::gemv_fusable(gbs, sg.K))
@@ -139,12 +144,16 @@ hipError_t norm_lm_head(const void* hidden, int dtype, const float* gamma, const
   const int layout = sg.layout;
   // the large-batch kernel combines straddling key groups into cleared entries
   uint32_t* gz = layout ? gkey : nullptr;
+  const bool fused = layout && fs && fs_dev;
   e = tail::launch_split(hidden, dtype, true, gamma, gbs, H, H_u, sg.K, ps, eps, deferred, sg.nt,
-                         layout, sg.rows_pad, sg.Kp, act, r, gz, (V + tail::kFusedGroup - 1) / tail::kFusedGroup, st);
+                         layout, sg.rows_pad, sg.Kp, act, r, gz,
+                         (V + tail::kFusedGroup - 1) / tail::kFusedGroup,
+                         fused ? *fs : tail::FusedSelect{}, fused ? fs_dev : nullptr, st);
   if (e != hipSuccess) return e;
   if (layout)
     return tail::launch_lm_head_rows(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
-                                     deferred ? r : nullptr, gbs, logits, gkey, st);
+                                     deferred ? r : nullptr, gbs, logits, gkey,
+                                     fused ? fs_dev : nullptr, st);
   return tail::launch_lm_head_mfma(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
                                    deferred ? r : nullptr, gbs, logits, gkey, part, st);
 }
@@ -224,10 +233,11 @@ TAIL_API int tail_lm_head(const float* y, const uint16_t* w_t, const float* row_
   uint16_t* act = (uint16_t*)ws;
   const int layout = sg.layout;
   hipError_t e = tail::launch_split(y, TAIL_F32, false, nullptr, gbs, H, H_u, sg.K, ps, 0.0f, false,
-                                    sg.nt, layout, sg.rows_pad, sg.Kp, act, nullptr, nullptr, 0, st);
+                                    sg.nt, layout, sg.rows_pad, sg.Kp, act, nullptr, nullptr, 0,
+                                    tail::FusedSelect{}, nullptr, st);
   if (e == hipSuccess)
     e = layout ? tail::launch_lm_head_rows(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
-                                           row_scale, gbs, logits, nullptr, st)
+                                           row_scale, gbs, logits, nullptr, nullptr, st)
                : tail::launch_lm_head_mfma(act, sg.nt, sg.rows_pad, sg.Kp, w_t, V, sg.K, ps,
                                            row_scale, gbs, logits, nullptr,
                                            (char*)ws + align256(sg.bytes), st);
@@ -256,7 +266,8 @@ TAIL_API int tail_rmsnorm_lm_head(const void* hidden, int dtype, const float* ga
   float* r = out_r ? out_r : (float*)(base + L.r);
   return hip_status(norm_lm_head(hidden, dtype, gamma, w_t, gbs, H, H_u, V, eps, ps, flags,
                                  (float*)(base + L.y), r, (uint16_t*)(base + L.act),
-                                 base + L.part, logits, nullptr, (hipStream_t)stream));
+                                 base + L.part, logits, nullptr, nullptr, nullptr,
+                                 (hipStream_t)stream));
 }
 
 namespace {
@@ -329,6 +340,26 @@ int check_forward(const void* hidden, int dtype, const float* gamma, const uint1
   return TAIL_OK;
 }
 
+// The top-k and sampler run in a launch of their own unless the environment
+// sets TAIL_FUSED_SELECT=1: then the large-batch lm_head kernel runs them
+// after a grid barrier (bitwise the same results, but measured slower: the
+// barrier costs what the kernel boundary does, and the select on 512 threads
+// takes longer than on 1024).  TAIL_FUSED_SPIN sets how often a workgroup
+// polls that barrier before it leaves the rows to the others (tests set it to
+// 0, so that the last workgroup to arrive selects every row).  Read at every
+// call.
+bool fused_select_enabled() {
+  const char* e = getenv("TAIL_FUSED_SELECT");
+  return e && e[0] == '1' && e[1] == '\0';
+}
+int fused_select_spin() {
+  constexpr int kDefaultSpin = 4096;  // a few ms of polling; the normal wait is tens of us
+  const char* e = getenv("TAIL_FUSED_SPIN");
+  if (!e || !*e) return kDefaultSpin;
+  const long v = strtol(e, nullptr, 10);
+  return v < 0 ? 0 : v > (1 << 24) ? (1 << 24) : int(v);
+}
+
 // The launches of tail_forward on a checked workspace of L.total bytes at ws.
 hipError_t forward_launch(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t,
                           int gbs, int H, int H_u, int V, int k, float eps, unsigned flags, int ps,
@@ -349,8 +380,20 @@ hipError_t forward_launch(const void* hidden, int dtype, const float* gamma, con
   const bool fold = flags & TAIL_NAN_FOLD;
   const bool fused_groups = g.gs == tail::kFusedGroup && !fold;
   uint32_t* gk_fused = fused_groups ? gk : nullptr;
+  // on the large-batch path with the epilogue's key groups, the lm_head
+  // kernel runs the top-k and sampler itself
+  const SplitGeom sg = split_geom(gbs, H, H_u, ps, V, flags);
+  const bool fused = fused_groups && gbs > tail::kGemvMaxBatch && sg.layout == 1 &&
+                     tail::rows_fuse_select(sg.nt, gbs) && fused_select_enabled();
+  tail::FusedSelect* fs_dev = (tail::FusedSelect*)(base + L.sync);
+  const tail::FusedSelect fs{vals,     idx,      params,
+                             ncols,    tokens,   k,
+                             g.gs,     g.groups, (uint32_t*)(base + L.sync + sizeof(tail::FusedSelect)),
+                             tail::fused_sync_words(gbs), fused_select_spin()};
   hipError_t e = norm_lm_head(hidden, dtype, gamma, w_t, gbs, H, H_u, V, eps, ps, flags, y, r, act,
-                              base + L.part, lg, gk_fused, st);
+                              base + L.part, lg, gk_fused, fused ? &fs : nullptr,
+                              fused ? fs_dev : nullptr, st);
+  if (fused) return e;
   if (e == hipSuccess && !fused_groups) e = tail::launch_group_max(lg, gbs, V, g, fold, gk, st);
   if (e == hipSuccess)
     e = tail::launch_select(lg, gbs, V, k, g, gk, flags & TAIL_PAGE_PRECISION, fold, vals, idx,

@@ -164,16 +164,40 @@ inline int mfma_layout(int gbs, int V, int Kp) {
 }
 inline int mfma_row_tile(int layout) { return layout ? 32 : 16; }
 
+// The top-k and sampler of every row, run by the large-batch lm_head after a
+// grid barrier (lm_head_rows.hip) instead of by a launch of their own.
+// Group size gs must be kFusedGroup (the epilogue's key groups), without the
+// NaN fold; mirror ranking follows the one-term (page-precision) kernels.
+// The producer (launch_split) stores it in device memory, where that kernel
+// reads it after its tiles (as kernel arguments it would hold registers
+// through the whole contraction), and clears the counters.
+struct FusedSelect {
+  float* vals;          // [gbs, k]
+  int32_t* idx;         // [gbs, k]
+  const float* params;  // [gbs, ncols] or NULL (no sampling)
+  int ncols;
+  int32_t* tokens;      // [gbs] (with params)
+  int k, gs, groups;
+  uint32_t* sync;       // 2 words per launch of 128 or 256 rows (fused_sync_words)
+  int nsync;            // fused_sync_words(gbs)
+  int spin;             // polls of the arrival counter before a workgroup leaves the rows to others
+};
+inline int fused_sync_words(int gbs) { return 2 * ((gbs + 127) / 128); }
+// whether the large-batch kernel that takes gbs rows of nt terms has the
+// select phase (not the one-term kernel above 128 rows)
+inline bool rows_fuse_select(int nt, int gbs) { return nt == 2 || gbs <= 128; }
+
 // Split (and, with norm, RMS-normalize) activations for the matrix-core path:
 // act holds nt * rows_pad * Kp bf16 bits over the K contraction lanes as 1 KB
 // MFMA operand fragments ordered (term, row tile, K block) in the given layout
 // (0: 16-row tiles and 32-lane K blocks for v_mfma_f32_16x16x32_bf16, 1:
 // 32-row tiles and 16-lane K blocks for v_mfma_f32_32x32x16_bf16); r [gbs]
-// (norm only, may be NULL); gz [gbs, groups] (may be NULL) is cleared.
+// (norm only, may be NULL); gz [gbs, groups] (may be NULL) is cleared; fs_out
+// (may be NULL, device memory): receives fs, and fs.sync [fs.nsync] is cleared.
 hipError_t launch_split(const void* src, int dtype, bool norm, const float* gamma, int gbs, int H,
                         int H_u, int K, int pad_s, float eps, bool deferred, int nt, int layout,
                         int rows_pad, int Kp, uint16_t* act, float* r, uint32_t* gz, int groups,
-                        hipStream_t st);
+                        const FusedSelect& fs, FusedSelect* fs_out, hipStream_t st);
 
 // Matrix-core lm_head; part_ws: mfma_part_bytes(gbs, Kp, V) bytes (256-byte
 // aligned) for the split-K partials of a narrow vocabulary.
@@ -184,10 +208,12 @@ hipError_t launch_lm_head_mfma(const uint16_t* act, int nt, int rows_pad, int Kp
 
 // The large-batch lm_head (layout 1 batches, see mfma_layout): act in layout 1 with
 // rows_pad a multiple of 32; gkey (may be NULL) must hold zeros where the
-// producer cleared it.
+// producer cleared it; fs (may be NULL; device memory the producer wrote):
+// also the rows' top-k and sampler.
 hipError_t launch_lm_head_rows(const uint16_t* act, int nt, int rows_pad, int Kp, const uint16_t* w,
                                int V, int K, int pad_s, const float* row_scale, int gbs,
-                               float* logits, uint32_t* gkey, hipStream_t st);
+                               float* logits, uint32_t* gkey, const FusedSelect* fs,
+                               hipStream_t st);
 
 // Split-K finish shared by the lm_head paths: logits[b, v] = row_scale[b] (or
 // 1) * sum over kc in order of part[kc][b][v]; gkey (may be NULL) as above.

@@ -244,6 +244,17 @@ int tail_sample(const float* vals, const int32_t* idx, int gbs, int k, const flo
  *   logits: [gbs, V] fp32, required only with TAIL_EMIT_LOGITS.
  *   vals, idx: [gbs, k] top-k outputs (always written).
  *   ws:     workspace of at least tail_workspace_size(...) bytes, 256-byte aligned.
+ *
+ * From 65 rows the lm_head kernel can also run the top-k and sampler itself,
+ * after a grid barrier, so that the step is the producer and one kernel (the
+ * page's fused tail; GPT-OSS tail API page, Background): the environment
+ * variable TAIL_FUSED_SELECT=1, read at every call, selects that, for
+ * batches whose top-k groups are the lm_head's 64-column groups and without
+ * TAIL_NAN_FOLD (and up to 128 rows in the page-precision mode).  The outputs
+ * are bitwise the same either way; it is not the default because it measured
+ * slower.  Its barrier waits a bounded time (TAIL_FUSED_SPIN polls, 4096 by
+ * default), after which a workgroup leaves its share of the rows to the
+ * others, so a call ends with every row done even where the GPU is shared.
  */
 int tail_forward(const void* hidden, int dtype, const float* gamma, const uint16_t* w_t, int gbs,
                  int H, int H_u, int V, int k, float eps, unsigned flags, const float* params,
