@@ -10,8 +10,9 @@ bf16 hidden, sampling at top_k 256, top_p 1, T 1, u 0.5, logits not emitted.
 `value` is tokens/s = gbs * K / (time of K steps), timed with HIP events on
 the stream the library launches on, bracketed by device synchronizations.
 
-Also reported: per-step p10/p50/p90, the step with logits emitted, per-stage
-times, the page-precision mode's step and lm_head (`page_precision`), the
+Also reported: per-step p10/p50/p90, the step with logits emitted, the
+gbs-256 step with the top-k and sampler fused into the lm_head kernel
+(`ms_per_step_fused_select`, an opt-in variant), per-stage times, the page-precision mode's step and lm_head (`page_precision`), the
 step on one vocabulary shard's shape (V / 8 columns, `vocab_shard_points`), the lm_head kernel's algorithmic HBM rate against the 8 TB/s peak
 (`roofline`), the same numbers at gbs 8 / 64 / 256 (`by_gbs`, with the
 matrix-core kernels' executed TFLOP/s against the 2.5 PFLOP/s dense bf16
@@ -71,6 +72,9 @@ def parse():
     ap.add_argument("--workload", default=None,
                     help="time only this workload label (for per-workload profiling runs)")
     ap.add_argument("--no-shard", action="store_true", help="skip the vocabulary-shard points")
+    ap.add_argument("--fused-select", choices=("auto", "off", "only"), default="auto",
+                    help="auto: also time the gbs-256 step with the top-k fused into the lm_head "
+                         "kernel; off: do not; only: fuse it in every step of the run (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -225,6 +229,15 @@ def bench_workload(cid, args, torch, np):
     t_emit = time_loop(torch, lambda: fe(g["hidden"], g["gamma"], g["w_t"], g["params"]),
                        max(10, args.steps // 4), args.warmup, settle_s=ss)
     del fe
+    fused_timed = inp.gbs >= 129 and args.fused_select == "auto"
+    if fused_timed:
+        # the same step with the top-k and sampler run by the large-batch
+        # lm_head kernel after its grid barrier (not the default: slower)
+        os.environ["TAIL_FUSED_SELECT"] = "1"
+        try:
+            t_fused = time_loop(torch, step, max(10, args.steps // 4), args.warmup, settle_s=ss)
+        finally:
+            os.environ.pop("TAIL_FUSED_SELECT", None)
     # stage by stage.  rmsnorm_lm_head runs the same kernels and launch shapes
     # as tail_forward's first stage (there they also emit the group maxima);
     # topk and sample are the standalone calls (inside tail_forward the group
@@ -253,6 +266,7 @@ def bench_workload(cid, args, torch, np):
                ms_per_step=t_step * 1e3, ms_p10_p50_p90_evented=[x * 1e3 for x in pct],
                settle_s_per_loop=ss,
                ms_per_step_emit_logits=t_emit * 1e3,
+               **(dict(ms_per_step_fused_select=t_fused * 1e3) if fused_timed else {}),
                stage_us=dict(rmsnorm_lm_head=t_lm * 1e6, topk=t_topk * 1e6, sample=t_samp * 1e6),
                lm_head_gbs=lm_bytes / t_lm / 1e9, lm_head_tflops=flops / t_lm / 1e12,
                lm_head_bytes=lm_bytes)
@@ -374,6 +388,8 @@ def main():
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the tail runs with the whole vocabulary on one device)", file=sys.stderr)
         sys.exit(2)
+    if args.fused_select == "only":
+        os.environ["TAIL_FUSED_SELECT"] = "1"  # the library reads it at every call
     import numpy as np
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
