@@ -274,7 +274,12 @@ __device__ __forceinline__ void fused_select(unsigned char* smem, int tid, const
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
+    // the explicit waits after the write-back and after the invalidation
+    // make each complete before the arrival, and before the other waves
+    // read (the compiler adds none there when no store or load of this wave
+    // is outstanding)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);
     uint32_t n = __hip_atomic_fetch_add(&sync[0], 1u, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT) + 1u;
     for (int i = 0; n < gridDim.x && i < fs.spin; ++i) {
@@ -283,6 +288,7 @@ __device__ __forceinline__ void fused_select(unsigned char* smem, int tid, const
     }
     *word = n >= gridDim.x;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(*word)) return;  // the rows are left to the others
