@@ -257,8 +257,9 @@ __device__ __forceinline__ void tile_part(const CP& cp, const lds_u8* wring, con
 
 // The grid barrier and the select phase (see above) over rows b0 .. b0 +
 // nrows - 1; smem holds at least a SelShared and one more word.  MIRROR: the
-// page-precision mode's bf16 ranking.  tid = 64 wave + lane (the tile phase
-// keeps both live, so no register of its own carries the work-item id).
+// page-precision mode's bf16 ranking.  tid = 64 wave + lane, the lane
+// recomputed from the execution mask (carrying the work-item id through the
+// tile phase would cost a register there).
 template <bool MIRROR>
 __device__ __forceinline__ void fused_select(unsigned char* smem, int tid, const FusedSelect& fs,
                                              uint32_t* sync, const float* logits,
