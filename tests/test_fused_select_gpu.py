@@ -7,7 +7,9 @@ kernel shapes (128-row and 256-row chunks), several launches per batch,
 the page-precision mirror ranking, every sampler width (k up to 1024), with
 and without emitted logits and sampling; with TAIL_FUSED_SPIN=0 no
 workgroup waits at the barrier, so the last one to arrive selects every row
-(the path a shared GPU takes when not all workgroups are resident).  A
+(the path a shared GPU takes when not all workgroups are resident), and with
+a limit of 2 polls some workgroups leave while others pass and share the
+rows.  A
 batch the fused kernel does not take (one-term above 128 rows) falls back
 to the separate launch unchanged."""
 import numpy as np
@@ -65,13 +67,16 @@ def assert_same(a, b, what):
 
 
 def run(monkeypatch, mode, f, args):
-    """mode: 'separate', 'fused' or 'fused_nowait'."""
+    """mode: 'separate', 'fused', 'fused_nowait' (no polling) or
+    'fused_short' (2 polls)."""
     monkeypatch.delenv("TAIL_FUSED_SELECT", raising=False)
     monkeypatch.delenv("TAIL_FUSED_SPIN", raising=False)
     if mode != "separate":
         monkeypatch.setenv("TAIL_FUSED_SELECT", "1")
     if mode == "fused_nowait":
         monkeypatch.setenv("TAIL_FUSED_SPIN", "0")
+    if mode == "fused_short":
+        monkeypatch.setenv("TAIL_FUSED_SPIN", "2")
     f.vals.fill_(float("nan"))
     f.idx.fill_(-1)
     f.tokens.fill_(-1)
@@ -102,7 +107,7 @@ def test_fused_select_bitwise_equal(monkeypatch, gbs, H, H_u, V, k, zp, page, em
             torch.from_numpy(p).cuda() if sample else None)
     f = dst.Forward(gbs, H, V, k, H_u, 1e-5, zp, True, emit, page=page)
     ref = run(monkeypatch, "separate", f, args)
-    for mode in ("fused", "fused_nowait", "fused"):
+    for mode in ("fused", "fused_nowait", "fused_short", "fused"):
         assert_same(run(monkeypatch, mode, f, args), ref, (mode, gbs, V, k))
 
 
