@@ -314,10 +314,11 @@ __device__ inline void for_candidates(const SelShared& s, const float* row, int 
 
 // Step b: append every element with key >= t0 to the LDS list.  Each thread
 // issues kScanBatch float4 loads at once and checks them together (a bit
-// mask).  Five per thread cover up to 320 candidate groups of 64 in one pass
-// (k = 256 rows of GPT-OSS hold about 265): the scan then took 4.6-5.1 us
-// against 5.1-5.8 us with four (two passes) and 6.1-6.5 us with eight (one
-// pass, but every thread checks 32 mostly empty slots).  The wave
+// mask).  With 1024 threads, five per thread cover up to 320 candidate groups
+// of 64 in one pass (k = 256 rows of GPT-OSS hold about 265): the scan then
+// took 4.6-5.1 us against 5.1-5.8 us with four (two passes) and 6.1-6.5 us
+// with eight (one pass, but every thread checks 32 mostly empty slots); 512
+// threads take two passes.  The wave
 // prefix-sums the counts with shuffles, and one LDS atomic per wave and batch
 // reserves the slots (none when the wave found nothing, the common case);
 // positions past kCap are counted but not stored.  Same elements, keys and
