@@ -194,3 +194,18 @@ def test_fused_select_noalloc(monkeypatch):
         f.vals.fill_(float("nan"))
         got = outputs(f, f.noalloc(*args))
         assert_same(got, ref, ("noalloc", gbs))
+
+
+@pytest.mark.parametrize("V,k,fold", [(16456, 256, True), (8200, 256, False)])
+def test_fused_select_falls_back(monkeypatch, V, k, fold):
+    """Batches the fused kernel does not take keep the separate launch under
+    TAIL_FUSED_SELECT=1: the NaN fold (its group maxima come from a pass of
+    their own), and top-k groups other than the lm_head's 64-column groups
+    (8200 columns hold 129 groups of 64, fewer than k = 256)."""
+    gbs, H = 200, 64
+    x, gamma, w, p = inputs(gbs, H, H, V, k, False, V + k)
+    args = (torch.from_numpy(x).cuda(), torch.from_numpy(gamma).cuda(), gpu_bf16(w),
+            torch.from_numpy(p).cuda())
+    f = dst.Forward(gbs, H, V, k, H, 1e-5, False, True, True, nan_fold=fold)
+    ref = run(monkeypatch, "separate", f, args)
+    assert_same(run(monkeypatch, "fused", f, args), ref, ("fallback", V, k, fold))
